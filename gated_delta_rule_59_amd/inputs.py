@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the KDA workloads.
+
+This module only draws random numbers and shapes them (normalise, squash,
+round to the storage dtype). It holds none of the recurrence's arithmetic, so
+both the HIP path and the CPU reference can consume what it makes.
+
+Workloads (shapes and distributions of the Kimi K3 KDA layer; see the
+"Eine Untergrenze, die einen GPU-Codepfad beseitigte" section of the orkas.ai
+Kimi K3 architecture page for the -5 floor on the per-step log-decay):
+
+  0  tiny-f32     B=1, H=2,  T=64,    dk=dv=32,  chunk 16, fp32 everything, S0 = 0
+  1  prefill-4k   B=1, H=16, T=4096,  dk=dv=128, chunk 64, bf16 activations, S0 ~ 0.02 N(0,1)
+  2  prefill-64k  B=1, H=32, T=65536, dk=dv=128, chunk 64, bf16, half of each head's key
+                  channels pinned at g = -5 + 1e-3 (bf16 rounds that to -5.0 exactly)
+  3  varlen-16    16 packed sequences, lengths uniform in [512, 16384], H=32, dk=dv=128, bf16
+  4  decode-512   N=512 sequences, H=32, dk=dv=128, fp32 state 0.02 N(0,1) (1 GiB), bf16 token
+                  inputs, a pool of 16 seeded step-input sets cycled over the steps
+
+Every array is produced in float32 and then rounded to the storage dtype; the
+float32 arrays returned hold exactly the values the kernels receive.
+Draw order per workload: (lengths) -> q -> k -> v -> beta -> g -> S0 -> (channel mask).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+GATE_FLOOR = -5.0          # per-step log-decay lower bound (retain >= e^-5 = 0.67 %)
+DECODE_POOL = 16           # distinct seeded step-input sets for the decode workload
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    r = (b + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+@dataclass
+class Workload:
+    name: str
+    wid: int
+    H: int
+    dk: int
+    dv: int
+    chunk: int
+    dtype: str                      # storage dtype of q, k, v, g, beta and o: "f32" | "bf16"
+    B: int = 1
+    T: int = 0                      # tokens per batch row (packed total when cu_seqlens is set)
+    lengths: Optional[list] = None  # varlen sequence lengths
+    n_seq: int = 1
+
+
+@dataclass
+class KDAInputs:
+    """q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H]; S0: [n_seq, H, dk, dv] or None.
+
+    cu_seqlens: int32 [n_seq + 1] token offsets into the packed T axis (B == 1), or None
+    for a dense batch of B sequences of length T.
+    """
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    S0: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray] = None
+    extra: dict = field(default_factory=dict)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def _unit_rows(x):
+    n = np.sqrt(np.sum(np.square(x, dtype=np.float64), axis=-1, keepdims=True))
+    return (x / n).astype(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def draw_activations(rng, B, T, H, dk, dv, dtype):
+    """q, k unit rows over dk; v ~ N(0,1); beta = sigmoid(N(0,1)); g = -5 sigmoid(N(0,1))."""
+    q = to_storage(_unit_rows(_normal(rng, (B, T, H, dk))), dtype)
+    k = to_storage(_unit_rows(_normal(rng, (B, T, H, dk))), dtype)
+    v = to_storage(_normal(rng, (B, T, H, dv)), dtype)
+    beta = to_storage(_sigmoid(_normal(rng, (B, T, H))), dtype)
+    g = to_storage(GATE_FLOOR * _sigmoid(_normal(rng, (B, T, H, dk))), dtype)
+    return q, k, v, g, beta
+
+
+def draw_state(rng, n, H, dk, dv, std=0.02):
+    return (std * _normal(rng, (n, H, dk, dv))).astype(np.float32)
+
+
+WORKLOADS = {
+    0: Workload("tiny-f32", 0, H=2, dk=32, dv=32, chunk=16, dtype="f32", B=1, T=64),
+    1: Workload("prefill-4k", 1, H=16, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=4096),
+    2: Workload("prefill-64k-bound", 2, H=32, dk=128, dv=128, chunk=64, dtype="bf16", B=1, T=65536),
+    3: Workload("varlen-16", 3, H=32, dk=128, dv=128, chunk=64, dtype="bf16", B=1, n_seq=16),
+    4: Workload("decode-512", 4, H=32, dk=128, dv=128, chunk=0, dtype="bf16", B=512, T=1, n_seq=512),
+}
+
+
+def make_prefill(wid: int, *, T: Optional[int] = None, H: Optional[int] = None,
+                 n_seq: Optional[int] = None) -> KDAInputs:
+    """Inputs of prefill workload `wid` (0..3). T / H / n_seq override the sizes for
+    reduced-size test cases (same distributions and structure, same seed)."""
+    base = WORKLOADS[wid]
+    wl = Workload(**{**base.__dict__})
+    if H is not None:
+        wl.H = H
+    rng = np.random.default_rng([0, wid])
+    cu = None
+    if wid == 3:
+        ns = n_seq if n_seq is not None else base.n_seq
+        lo, hi = (512, 16384) if T is None else (max(1, T // 4), T)
+        lens = rng.integers(lo, hi, size=ns, endpoint=True).astype(np.int64)
+        wl.lengths = [int(x) for x in lens]
+        wl.n_seq = ns
+        wl.T = int(lens.sum())
+        cu = np.zeros(ns + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lens)
+    elif T is not None:
+        wl.T = T
+    q, k, v, g, beta = draw_activations(rng, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype)
+    S0 = None
+    if wid != 0:
+        S0 = draw_state(rng, wl.n_seq if wid == 3 else wl.B, wl.H, wl.dk, wl.dv)
+    extra = {}
+    if wid == 2:
+        pinned = np.zeros((wl.H, wl.dk), dtype=bool)
+        for h in range(wl.H):
+            pinned[h, rng.permutation(wl.dk)[: wl.dk // 2]] = True
+        g[:, :, pinned] = to_storage(np.float32(GATE_FLOOR + 1e-3), wl.dtype)
+        extra["pinned_channels"] = pinned
+    return KDAInputs(wl, q, k, v, g, beta, S0, cu, extra)
+
+
+def make_decode_state(N: int = 512, H: int = 32, dk: int = 128, dv: int = 128) -> np.ndarray:
+    """Decode workload state: fp32 [N, H, dk, dv] ~ 0.02 N(0,1) (1 GiB at the full size)."""
+    rng = np.random.default_rng([0, 4])
+    return draw_state(rng, N, H, dk, dv)
+
+
+def make_decode_step(p: int, N: int = 512, H: int = 32, dk: int = 128, dv: int = 128):
+    """Step-input set p of the decode workload: q, k, g [N, H, dk], v [N, H, dv], beta [N, H]
+    in bf16 values, drawn as for prefill-4k. Step s of a run uses set s % DECODE_POOL."""
+    rng = np.random.default_rng([0, 4, 1 + p])
+    q, k, v, g, beta = draw_activations(rng, N, 1, H, dk, dv, "bf16")
+    return q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
