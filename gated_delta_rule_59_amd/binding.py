@@ -1,0 +1,212 @@
+"""Python binding of libkda (include/kda.h): torch tensors in, device pointers and the
+current HIP stream out to the C ABI. Argument marshalling only; every step of the
+computation runs in the library's kernels. Raises if the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_FLAG_GENERIC = 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
+          4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_DECAY_RANGE", 6: "KDA_ERR_WORKSPACE",
+          7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
+
+_P = ctypes.c_void_p
+
+
+class ChunkArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("cu_seqlens", _P), ("N", ctypes.c_int),
+                ("act_dtype", ctypes.c_int), ("gate_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+                ("S0", _P), ("o", _P), ("S_T", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int),
+                ("act_dtype", ctypes.c_int), ("gate_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+                ("S", _P), ("o", _P)]
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkda is not built ({LIB_PATH} missing); run "
+                               "python -m gated_delta_rule_59_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kda_chunk_fwd_workspace.argtypes = [ctypes.POINTER(ChunkArgs),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.kda_chunk_fwd_workspace.restype = ctypes.c_int
+        L.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkArgs), _P]
+        L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_check_gates.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int, _P,
+                                      ctypes.POINTER(ctypes.c_int64)]
+        L.kda_check_gates.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_abi_version.argtypes = []
+        L.kda_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KDAError(status, lib().kda_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _P(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream) -> _P:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _P(s.cuda_stream)
+
+
+def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, S_T=None,
+               workspace=None, generic=False) -> ChunkArgs:
+    B, T, H, dk = q.shape
+    a = ChunkArgs()
+    a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, v.shape[-1], chunk
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.N = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.act_dtype = _dtype_code(q.dtype)
+    a.gate_dtype = _dtype_code(g.dtype)
+    a.out_dtype = _dtype_code(o.dtype) if o is not None else KDA_F32
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(t) for t in (q, k, v, g, beta))
+    a.S0, a.o, a.S_T = _ptr(S0), _ptr(o), _ptr(S_T)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.flags = KDA_FLAG_GENERIC if generic else 0
+    return a
+
+
+def chunk_fwd_workspace_bytes(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
+                              generic=False) -> int:
+    a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, generic=generic)
+    n = ctypes.c_size_t(0)
+    _check(lib().kda_chunk_fwd_workspace(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """Device scratch for kda_chunk_fwd (torch's allocator returns 256-byte aligned blocks)."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
+              out_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None,
+              generic=False, stream=None):
+    """Prefill. q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H] (bf16 or fp32, on the
+    GPU, contiguous); S0 [n_seq, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] or None.
+    Returns (o [B, T, H, dv] out_dtype, S_T [n_seq, H, dk, dv] fp32 or None).
+    S_T may be passed as S0 itself to continue in place."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _dev(t, name)
+    if S0 is not None:
+        _dev(S0, "S0")
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    else:
+        _dev(o, "o")
+    if S_T is None and want_state:
+        S_T = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = chunk_fwd_workspace_bytes(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk,
+                                           generic=generic)
+        workspace = alloc_workspace(nbytes, q.device)
+    a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
+                   workspace=workspace, generic=generic)
+    _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
+    return o, S_T
+
+
+def decode_args(q, k, v, g, beta, S, o) -> DecodeArgs:
+    N, H, dk = q.shape
+    a = DecodeArgs()
+    a.N, a.H, a.dk, a.dv = N, H, dk, v.shape[-1]
+    a.act_dtype = _dtype_code(q.dtype)
+    a.gate_dtype = _dtype_code(g.dtype)
+    a.out_dtype = _dtype_code(o.dtype)
+    a.q, a.k, a.v, a.g, a.beta, a.S, a.o = (_ptr(t) for t in (q, k, v, g, beta, S, o))
+    return a
+
+
+def decode_step(q, k, v, g, beta, S, *, o=None, out_dtype=torch.float32, stream=None):
+    """One token per sequence: q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H]; S [N, H, dk, dv]
+    fp32 updated in place. Returns o [N, H, dv]."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S", S)):
+        _dev(t, name)
+    if o is None:
+        o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=out_dtype, device=q.device)
+    a = decode_args(q, k, v, g, beta, S, o)
+    _check(lib().kda_decode_step(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def check_gates(g, beta, stream=None) -> int:
+    """Number of g values outside [-5, 0] plus beta values outside [0, 1] (synchronises)."""
+    _dev(g, "g")
+    _dev(beta, "beta")
+    n = ctypes.c_int64(0)
+    _check(lib().kda_check_gates(_ptr(g), g.numel(), _ptr(beta), beta.numel(),
+                                 _dtype_code(g.dtype), _stream(stream), ctypes.byref(n)))
+    return int(n.value)

@@ -1,0 +1,248 @@
+// libkda C ABI: argument validation, path selection, workspace sizing and launches.
+// Every check happens on the host before anything is enqueued; see include/kda.h.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kda_status ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
+size_t dsize(kda_dtype t) { return t == KDA_F32 ? 4 : 2; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{name, a, a + bytes};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+bool env_check() {
+  const char* s = std::getenv("KDA_CHECK");
+  return s && s[0] == '1';
+}
+
+kda_status run_gate_check(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
+                          kda_dtype dt, hipStream_t stream, int64_t* n_bad) {
+  const int nb = kda::check_blocks();
+  int64_t* counts = nullptr;
+  if (hipMalloc(&counts, sizeof(int64_t) * nb) != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_check_gates: hipMalloc of %d counters failed", nb);
+  hipError_t e = kda::launch_check_gates(g, n_g, beta, n_beta, dt == KDA_BF16, counts, stream);
+  std::vector<int64_t> host(nb, 0);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host.data(), counts, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  (void)hipFree(counts);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_check_gates: %s", hipGetErrorString(e));
+  int64_t total = 0;
+  for (int64_t c : host) total += c;
+  *n_bad = total;
+  return ok();
+}
+
+// Shape/dtype validation shared by kda_chunk_fwd and kda_chunk_fwd_workspace.
+kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
+  if (!a) return fail(KDA_ERR_NULL_PTR, "args is NULL");
+  if (a->B < 1 || a->T < 0 || a->H < 1)
+    return fail(KDA_ERR_BAD_SHAPE, "need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", a->B, a->T,
+                a->H);
+  if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv))
+    return fail(KDA_ERR_BAD_SHAPE, "dk and dv must be 32, 64 or 128 (got %d, %d)", a->dk, a->dv);
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
+    return fail(KDA_ERR_BAD_SHAPE, "chunk must be 16, 32 or 64 (got %d)", a->chunk);
+  if (a->cu_seqlens) {
+    if (a->B != 1) return fail(KDA_ERR_BAD_SHAPE, "cu_seqlens requires B == 1 (got %d)", a->B);
+    if (a->N < 1) return fail(KDA_ERR_BAD_SHAPE, "cu_seqlens requires N >= 1 (got %d)", a->N);
+  }
+  if (!dtype_ok(a->act_dtype) || !dtype_ok(a->gate_dtype) || !dtype_ok(a->out_dtype))
+    return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
+  if (a->act_dtype != a->gate_dtype)
+    return fail(KDA_ERR_BAD_DTYPE, "act_dtype and gate_dtype must match (both F32 or both BF16)");
+  if (a->flags & ~KDA_FLAG_GENERIC) return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags);
+  const int64_t tokens = (int64_t)a->B * a->T;
+  const int n_seq = a->cu_seqlens ? a->N : a->B;
+  if (tokens * a->H * (int64_t)(a->dk > a->dv ? a->dk : a->dv) > (int64_t(1) << 40))
+    return fail(KDA_ERR_BAD_SHAPE, "problem too large");
+  if ((int64_t)n_seq * a->H * (a->dv / 16) > 0x7fffffffLL)
+    return fail(KDA_ERR_BAD_SHAPE, "too many (sequence, head) pairs");
+  *p = kda::ChunkPlan{a->B, a->T, a->H, a->dk, a->dv, a->chunk, a->cu_seqlens, n_seq,
+                      a->act_dtype == KDA_BF16, a->out_dtype == KDA_BF16,
+                      a->q, a->k, a->v, a->g, a->beta, a->S0, a->o, a->S_T,
+                      a->workspace, a->workspace_bytes};
+  return KDA_OK;
+}
+
+bool use_fast(const kda_chunk_args* a, const kda::ChunkPlan& p) {
+  return !(a->flags & KDA_FLAG_GENERIC) && kda::fast_path_applies(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_workspace(const kda_chunk_args* a, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_NULL_PTR, "bytes is NULL");
+  kda::ChunkPlan p;
+  kda_status s = validate_chunk_shapes(a, &p);
+  if (s != KDA_OK) return s;
+  *bytes = use_fast(a, p) ? kda::fast_workspace_bytes(p) : 0;
+  return ok();
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
+  kda::ChunkPlan p;
+  kda_status s = validate_chunk_shapes(a, &p);
+  if (s != KDA_OK) return s;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)
+    return fail(KDA_ERR_NULL_PTR, "q, k, v, g, beta and o must be non-NULL");
+  const size_t es = dsize(a->act_dtype), os = dsize(a->out_dtype);
+  const size_t tok = (size_t)a->B * a->T * a->H;
+  const size_t st = (size_t)p.n_seq * a->H * a->dk * a->dv * 4;
+  const Range in[] = {range("q", a->q, tok * a->dk * es), range("k", a->k, tok * a->dk * es),
+                      range("v", a->v, tok * a->dv * es), range("g", a->g, tok * a->dk * es),
+                      range("beta", a->beta, tok * es),
+                      range("S0", a->S0, a->S0 ? st : 0),
+                      range("cu_seqlens", a->cu_seqlens,
+                            a->cu_seqlens ? sizeof(int32_t) * (a->N + 1) : 0)};
+  const Range o = range("o", a->o, tok * a->dv * os);
+  const Range sT = range("S_T", a->S_T, a->S_T ? st : 0);
+  for (const Range& r : in)
+    if (overlap(o, r)) return fail(KDA_ERR_ALIAS, "o overlaps %s", r.name);
+  for (const Range& r : in) {
+    if (!overlap(sT, r)) continue;
+    if (std::strcmp(r.name, "S0") == 0 && a->S_T == a->S0) continue;  // in-place continue
+    return fail(KDA_ERR_ALIAS, "S_T overlaps %s", r.name);
+  }
+  if (overlap(sT, o)) return fail(KDA_ERR_ALIAS, "S_T overlaps o");
+
+  const bool fast = use_fast(a, p);
+  if (fast) {
+    const size_t need = kda::fast_workspace_bytes(p);
+    if (need && (!a->workspace || a->workspace_bytes < need))
+      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
+      return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const Range ws = range("workspace", a->workspace, need);
+    for (const Range& r : in)
+      if (overlap(ws, r)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", r.name);
+    if (overlap(ws, o) || overlap(ws, sT)) return fail(KDA_ERR_ALIAS, "workspace overlaps an output");
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (env_check()) {
+    int64_t bad = 0;
+    s = run_gate_check(a->g, (int64_t)(tok * a->dk), a->beta, (int64_t)tok, a->gate_dtype, stream,
+                       &bad);
+    if (s != KDA_OK) return s;
+    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
+  }
+  const hipError_t e = fast ? kda::launch_chunk_fast(p, stream) : kda::launch_chunk_generic(p, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_decode_step(const kda_decode_args* a, void* hip_stream) {
+  if (!a) return fail(KDA_ERR_NULL_PTR, "args is NULL");
+  if (a->N < 1 || a->H < 1)
+    return fail(KDA_ERR_BAD_SHAPE, "need N >= 1 and H >= 1 (got N=%d H=%d)", a->N, a->H);
+  if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv))
+    return fail(KDA_ERR_BAD_SHAPE, "dk and dv must be 32, 64 or 128 (got %d, %d)", a->dk, a->dv);
+  if ((int64_t)a->N * a->H > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "N * H too large");
+  if (!dtype_ok(a->act_dtype) || !dtype_ok(a->gate_dtype) || !dtype_ok(a->out_dtype))
+    return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
+  if (a->act_dtype != a->gate_dtype)
+    return fail(KDA_ERR_BAD_DTYPE, "act_dtype and gate_dtype must match (both F32 or both BF16)");
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->S || !a->o)
+    return fail(KDA_ERR_NULL_PTR, "q, k, v, g, beta, S and o must be non-NULL");
+  const size_t es = dsize(a->act_dtype), os = dsize(a->out_dtype);
+  const size_t nh = (size_t)a->N * a->H;
+  const Range in[] = {range("q", a->q, nh * a->dk * es), range("k", a->k, nh * a->dk * es),
+                      range("v", a->v, nh * a->dv * es), range("g", a->g, nh * a->dk * es),
+                      range("beta", a->beta, nh * es)};
+  const Range S = range("S", a->S, nh * a->dk * a->dv * 4);
+  const Range o = range("o", a->o, nh * a->dv * os);
+  for (const Range& r : in) {
+    if (overlap(o, r)) return fail(KDA_ERR_ALIAS, "o overlaps %s", r.name);
+    if (overlap(S, r)) return fail(KDA_ERR_ALIAS, "S overlaps %s", r.name);
+  }
+  if (overlap(S, o)) return fail(KDA_ERR_ALIAS, "S overlaps o");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (env_check()) {
+    int64_t bad = 0;
+    kda_status s = run_gate_check(a->g, (int64_t)(nh * a->dk), a->beta, (int64_t)nh,
+                                  a->gate_dtype, stream, &bad);
+    if (s != KDA_OK) return s;
+    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
+  }
+  const kda::DecodePlan p{a->N, a->H, a->dk, a->dv, a->act_dtype == KDA_BF16,
+                          a->out_dtype == KDA_BF16, a->q, a->k, a->v, a->g, a->beta, a->S, a->o};
+  const hipError_t e = kda::launch_decode(p, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_decode_step launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
+                           kda_dtype gate_dtype, void* hip_stream, int64_t* n_bad) {
+  if (!n_bad) return fail(KDA_ERR_NULL_PTR, "n_bad is NULL");
+  if (n_g < 0 || n_beta < 0) return fail(KDA_ERR_BAD_SHAPE, "negative element count");
+  if ((n_g && !g) || (n_beta && !beta)) return fail(KDA_ERR_NULL_PTR, "g or beta is NULL");
+  if (!dtype_ok(gate_dtype)) return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
+  return run_gate_check(g, n_g, beta, n_beta, gate_dtype, static_cast<hipStream_t>(hip_stream),
+                        n_bad);
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL_PTR: return "KDA_ERR_NULL_PTR";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE";
+    case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_DECAY_RANGE: return "KDA_ERR_DECAY_RANGE";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

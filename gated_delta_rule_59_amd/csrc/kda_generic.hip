@@ -1,0 +1,216 @@
+// Generic chunked KDA forward: fp32 arithmetic on the vector ALUs.
+//
+// Serves fp32 activations (where operand rounding to 16-bit formats would exceed a 1e-4
+// relative error budget) and every (dk, dv, chunk) the matrix-core path does not take.
+// Correct first; the fast path lives in kda_fast.hip.
+//
+// Chunked algebra (derived from the recurrence S_r = (I - b_r k_r k_r^T) D_r S_{r-1}
+// + b_r k_r v_r^T): for a chunk entered with state S and G_r = sum_{j<=r} g_j per key
+// channel,
+//     (I + A) U' = diag(b) (V - (K * e^G) S),   A[r][j] = b_r sum_c k_r[c] k_j[c] e^{G_r[c]-G_j[c]}, j < r
+//     O = (Q * e^G) S + Aqk U',                 Aqk[r][j] = sum_c q_r[c] k_j[c] e^{G_r[c]-G_j[c]}, j <= r
+//     S <- Diag(e^{G_C}) S + (K * e^{G_C - G})^T U'.
+// Here each e^{G_r - G_j} is evaluated from the difference directly: it never exceeds 1,
+// so no factor can overflow and no tiling of the exponent is needed on this path.
+//
+// One 256-thread workgroup per (sequence, head, 16 value columns); the state slice
+// S[dk][16] stays in LDS for the whole sequence.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kDVS = 16;  // value columns per workgroup
+
+struct GenericLds {
+  int off_k, off_q, off_g, off_a, off_aq, off_v, off_u, off_o, off_s, off_b, bytes;
+};
+
+__host__ __device__ inline GenericLds generic_lds(int C, int dk) {
+  GenericLds L;
+  int o = 0;
+  L.off_k = o; o += C * dk;
+  L.off_q = o; o += C * dk;
+  L.off_g = o; o += C * dk;
+  L.off_a = o; o += C * C;
+  L.off_aq = o; o += C * C;
+  L.off_v = o; o += C * kDVS;
+  L.off_u = o; o += C * kDVS;
+  L.off_o = o; o += C * kDVS;
+  L.off_s = o; o += dk * kDVS;
+  L.off_b = o; o += C;
+  L.bytes = o * 4;
+  return L;
+}
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void chunk_generic_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const TIn* __restrict__ g, const TIn* __restrict__ beta, const float* __restrict__ S0,
+    TOut* __restrict__ o, float* __restrict__ S_T, const int32_t* __restrict__ cu_seqlens,
+    int T, int H, int dk, int dv, int C, int n_seq) {
+  extern __shared__ float lds[];
+  const GenericLds L = generic_lds(C, dk);
+  float* Ks = lds + L.off_k;
+  float* Qs = lds + L.off_q;
+  float* Gs = lds + L.off_g;
+  float* Am = lds + L.off_a;
+  float* Aq = lds + L.off_aq;
+  float* Vs = lds + L.off_v;
+  float* Us = lds + L.off_u;
+  float* Os = lds + L.off_o;
+  float* Ss = lds + L.off_s;
+  float* Bs = lds + L.off_b;
+
+  const int n_slices = dv / kDVS;
+  const int slice = blockIdx.x % n_slices;
+  const int h = (blockIdx.x / n_slices) % H;
+  const int n = blockIdx.x / (n_slices * H);
+  if (n >= n_seq) return;
+  const int col0 = slice * kDVS;
+  const int tid = threadIdx.x;
+
+  int64_t tok0, len;
+  if (cu_seqlens) {  // clamped into [0, T] so a malformed table cannot index out of bounds
+    const int64_t a = min(max((int64_t)cu_seqlens[n], (int64_t)0), (int64_t)T);
+    const int64_t e = min(max((int64_t)cu_seqlens[n + 1], a), (int64_t)T);
+    tok0 = a;
+    len = e - a;
+  } else {
+    tok0 = (int64_t)n * T;
+    len = T;
+  }
+
+  const int64_t s_base = ((int64_t)n * H + h) * dk * dv;
+  for (int i = tid; i < dk * kDVS; i += 256) {
+    const int c = i / kDVS, j = i % kDVS;
+    Ss[i] = S0 ? S0[s_base + (int64_t)c * dv + col0 + j] : 0.f;
+  }
+
+  for (int64_t t0 = 0; t0 < len; t0 += C) {
+    const int Cn = (int)min((int64_t)C, len - t0);
+    __syncthreads();
+    // ---- load the chunk (rows past the sequence end: k = q = 0, g = 0, beta = 0)
+    for (int i = tid; i < C * dk; i += 256) {
+      const int r = i / dk, c = i % dk;
+      float kv = 0.f, qv = 0.f, gv = 0.f;
+      if (r < Cn) {
+        const int64_t e = ((tok0 + t0 + r) * H + h) * dk + c;
+        kv = ld(k, e);
+        qv = ld(q, e);
+        gv = ld(g, e);
+      }
+      Ks[i] = kv;
+      Qs[i] = qv;
+      Gs[i] = gv;
+    }
+    for (int i = tid; i < C * kDVS; i += 256) {
+      const int r = i / kDVS, j = i % kDVS;
+      Vs[i] = (r < Cn) ? ld(v, ((tok0 + t0 + r) * H + h) * dv + col0 + j) : 0.f;
+    }
+    for (int r = tid; r < C; r += 256) Bs[r] = (r < Cn) ? ld(beta, (tok0 + t0 + r) * H + h) : 0.f;
+    __syncthreads();
+    // ---- G = inclusive cumulative sum of g down the chunk, per key channel
+    for (int c = tid; c < dk; c += 256) {
+      float acc = 0.f;
+      for (int r = 0; r < C; ++r) {
+        acc += Gs[r * dk + c];
+        Gs[r * dk + c] = acc;
+      }
+    }
+    __syncthreads();
+    // ---- A (strictly lower, rows scaled by beta), Aqk (lower incl. diagonal)
+    for (int i = tid; i < C * C; i += 256) {
+      const int r = i / C, j = i % C;
+      float ak = 0.f, aq = 0.f;
+      if (j <= r) {
+        for (int c = 0; c < dk; ++c) {
+          const float e = __expf(Gs[r * dk + c] - Gs[j * dk + c]);
+          const float kj = Ks[j * dk + c] * e;
+          ak += Ks[r * dk + c] * kj;
+          aq += Qs[r * dk + c] * kj;
+        }
+      }
+      Am[i] = (j < r) ? Bs[r] * ak : 0.f;
+      Aq[i] = aq;
+    }
+    // ---- right-hand side diag(b)(V - Kbar S) into Us, and Qbar S into Os
+    for (int i = tid; i < C * kDVS; i += 256) {
+      const int r = i / kDVS, j = i % kDVS;
+      float ks = 0.f, qs = 0.f;
+      for (int c = 0; c < dk; ++c) {
+        const float e = __expf(Gs[r * dk + c]);
+        const float s = Ss[c * kDVS + j];
+        ks += Ks[r * dk + c] * e * s;
+        qs += Qs[r * dk + c] * e * s;
+      }
+      Us[i] = Bs[r] * (Vs[i] - ks);
+      Os[i] = qs;
+    }
+    __syncthreads();
+    // ---- forward substitution (I + A) U' = rhs, one value column per thread
+    if (tid < kDVS) {
+      const int j = tid;
+      for (int r = 1; r < C; ++r) {
+        float acc = Us[r * kDVS + j];
+        for (int m = 0; m < r; ++m) acc -= Am[r * C + m] * Us[m * kDVS + j];
+        Us[r * kDVS + j] = acc;
+      }
+    }
+    __syncthreads();
+    // ---- outputs of the chunk, then the state carried to the next chunk
+    for (int i = tid; i < C * kDVS; i += 256) {
+      const int r = i / kDVS, j = i % kDVS;
+      if (r < Cn) {
+        float acc = Os[i];
+        for (int m = 0; m <= r; ++m) acc += Aq[r * C + m] * Us[m * kDVS + j];
+        st(o, ((tok0 + t0 + r) * H + h) * dv + col0 + j, acc);
+      }
+    }
+    for (int i = tid; i < dk * kDVS; i += 256) {
+      const int c = i / kDVS, j = i % kDVS;
+      const float gC = Gs[(C - 1) * dk + c];
+      float acc = __expf(gC) * Ss[i];
+      for (int r = 0; r < C; ++r)
+        acc += Ks[r * dk + c] * __expf(gC - Gs[r * dk + c]) * Us[r * kDVS + j];
+      Ss[i] = acc;
+    }
+  }
+  __syncthreads();
+  if (S_T) {
+    for (int i = tid; i < dk * kDVS; i += 256) {
+      const int c = i / kDVS, j = i % kDVS;
+      S_T[s_base + (int64_t)c * dv + col0 + j] = Ss[i];
+    }
+  }
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_generic_t(const ChunkPlan& p, hipStream_t stream) {
+  const GenericLds L = generic_lds(p.chunk, p.dk);
+  auto kern = chunk_generic_kernel<TIn, TOut>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, L.bytes);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (int64_t)p.n_seq * p.H * (p.dv / kDVS);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), L.bytes, stream,
+                     static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
+                     static_cast<const TIn*>(p.v), static_cast<const TIn*>(p.g),
+                     static_cast<const TIn*>(p.beta), p.S0, static_cast<TOut*>(p.o), p.S_T,
+                     p.cu_seqlens, p.T, p.H, p.dk, p.dv, p.chunk, p.n_seq);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_generic(const ChunkPlan& p, hipStream_t stream) {
+  if (p.act_bf16)
+    return p.out_bf16 ? launch_generic_t<uint16_t, uint16_t>(p, stream)
+                      : launch_generic_t<uint16_t, float>(p, stream);
+  return p.out_bf16 ? launch_generic_t<float, uint16_t>(p, stream)
+                    : launch_generic_t<float, float>(p, stream);
+}
+
+}  // namespace kda

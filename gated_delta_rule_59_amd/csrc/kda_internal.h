@@ -1,0 +1,49 @@
+// Host-side launch descriptions passed from the C ABI layer (kda_api.cpp) to the kernel
+// launchers. Arguments are validated before a plan is built.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodePlan {
+  int N, H, dk, dv;
+  bool act_bf16, out_bf16;
+  const void *q, *k, *v, *g, *beta;
+  float* S;
+  void* o;
+};
+
+struct ChunkPlan {
+  int B, T, H, dk, dv, chunk;
+  const int32_t* cu_seqlens;  // device, or nullptr for a dense batch
+  int n_seq;                  // B (dense) or N (packed)
+  bool act_bf16, out_bf16;
+  const void *q, *k, *v, *g, *beta;
+  const float* S0;
+  void* o;
+  float* S_T;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
+
+// Generic path: fp32 arithmetic on the vector ALUs, any supported dk/dv/chunk; used for
+// fp32 activations and for shapes the matrix-core path does not take.
+hipError_t launch_chunk_generic(const ChunkPlan& p, hipStream_t stream);
+
+// Matrix-core path: bf16 activations, dk = dv = 128, chunk = 64.
+bool fast_path_applies(const ChunkPlan& p);
+size_t fast_workspace_bytes(const ChunkPlan& p);
+hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream);
+
+// Device check of g in [-5, 0] and beta in [0, 1]; writes per-block counts of violations
+// into counts[0 .. n_blocks) (n_blocks = check_blocks()).
+int check_blocks();
+hipError_t launch_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
+                              bool bf16, int64_t* counts, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,149 @@
+/* libkda: Kimi Delta Attention (KDA) on AMD MI355X (gfx950). C ABI.
+ *
+ * KDA is the fixed-size-state linear-attention layer of Kimi K3 (the "Sequenz" section of
+ * the orkas.ai Kimi K3 architecture page: a running state of fixed size that decays, so
+ * newer tokens weigh more). Per (sequence, head) the state S is a dk x dv fp32 matrix,
+ * rows indexed by key channel, and each token t does
+ *
+ *     S <- Diag(exp(g_t)) S;   u = v_t - S^T k_t;   S <- S + beta_t k_t u^T;   o_t = S^T q_t
+ *
+ * i.e. the incoming state goes through a token-dependent transition before the write,
+ * which is why per-device states cannot simply be summed (same page, section
+ * "Die Rechnung landet in der Bereitstellungsinfrastruktur").
+ *
+ * Two calls:
+ *   kda_chunk_fwd    - prefill: the whole sequence(s), chunkwise parallel. Chunks are split
+ *                      into 16-token tiles whose cumulative log-decay stays in [-80, 0]
+ *                      because each step's log-decay is >= -5 (section "Eine Untergrenze,
+ *                      die einen GPU-Codepfad beseitigte"), so the diagonal tiles use the
+ *                      same dense matrix products as all the others.
+ *   kda_decode_step  - one new token per sequence; the state is updated in place and the
+ *                      work does not grow with the context (studioglobal.ai Kimi K3 pages,
+ *                      "KDA haandterer den vedvarende sekvensbehandling" and "Architektur fuer
+ *                      lange Kontexte und guenstigeres Decoding"; orkas.ai infrastructure
+ *                      section: the state is updated in place).
+ *
+ * Conventions shared by every call
+ *   - Pointers named q, k, v, g, beta, o, S0, S_T, S, workspace, cu_seqlens are DEVICE
+ *     pointers (hipMalloc'ed or torch tensors); argument structs live in host memory.
+ *   - The caller allocates and owns every buffer. The library keeps no device memory and
+ *     no global mutable state other than a per-thread error string; it is thread safe.
+ *   - Every call validates its arguments on the host, before any launch, and returns a
+ *     kda_status. On failure nothing has been enqueued and kda_last_error() describes why.
+ *   - Work is enqueued on the caller's HIP stream (NULL = the default stream) and the call
+ *     returns without synchronising. Launch failures are reported as KDA_ERR_HIP.
+ *   - Nothing is printed and no exception crosses the ABI.
+ *   - Preconditions not checked by default: g in [-5, 0], beta in [0, 1], q and k rows of
+ *     unit L2 norm. With the environment variable KDA_CHECK=1, kda_chunk_fwd and
+ *     kda_decode_step first run a device check of g and beta, synchronise the stream and
+ *     return KDA_ERR_DECAY_RANGE if any value is outside its range. Nothing is clamped.
+ *   - Layout: token-major, [B, T, H, d] contiguous (d fastest). States [n_seq, H, dk, dv]
+ *     fp32 row-major (key channel rows, value channel columns).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,    /* sizes out of range or inconsistent */
+    KDA_ERR_BAD_DTYPE = 3,    /* dtype combination not offered */
+    KDA_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement */
+    KDA_ERR_DECAY_RANGE = 5,  /* KDA_CHECK=1 found g outside [-5, 0] or beta outside [0, 1] */
+    KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than kda_chunk_fwd_workspace() */
+    KDA_ERR_HIP = 7,          /* a HIP runtime call or kernel launch failed */
+    KDA_ERR_ALIAS = 8         /* an output overlaps an input it must not overlap */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Arguments of kda_chunk_fwd (prefill).
+ *
+ *   B, T       dense batch: B sequences of T tokens each. With cu_seqlens: B must be 1 and
+ *              T is the packed total length.
+ *   H          heads (independent).
+ *   dk, dv     key and value head dims, each in {32, 64, 128}.
+ *   chunk      chunk length in {16, 32, 64}; a performance knob (results agree across
+ *              chunk lengths to rounding). Each chunk is processed as 16-token tiles.
+ *   cu_seqlens device int32 [N + 1], token offsets of N packed sequences (0 = cu[0] <= ...
+ *              <= cu[N] = T), or NULL for the dense batch. Chunks never straddle a sequence
+ *              boundary and each sequence starts from its own S0[n].
+ *   N          number of packed sequences (ignored when cu_seqlens is NULL; n_seq = B then).
+ *   act_dtype  dtype of q, k, v.   gate_dtype  dtype of g, beta.   out_dtype  dtype of o.
+ *              Offered: act = gate = BF16 or act = gate = F32; out F32 or BF16.
+ *   q, k, g    [B, T, H, dk];  v [B, T, H, dv];  beta [B, T, H].  Read only.
+ *              g is the natural-log per-step decay of each key channel, beta the write
+ *              strength.
+ *   S0         [n_seq, H, dk, dv] fp32 initial states, or NULL for zeros.
+ *   o          [B, T, H, dv] out_dtype. Written. Must not overlap any input.
+ *   S_T        [n_seq, H, dk, dv] fp32 final states, or NULL. May be the same buffer as S0
+ *              (continue in place); must not partially overlap it.
+ *   workspace  device scratch of at least kda_chunk_fwd_workspace() bytes (may be NULL
+ *              when that is 0), 256-byte aligned; contents on entry are ignored.
+ *   flags      0, or KDA_FLAG_GENERIC to force the fp32 vector-ALU path (needs no
+ *              workspace; slower; used to cross-check the matrix-core path).
+ */
+typedef struct {
+    int B, T, H, dk, dv, chunk;
+    const int32_t* cu_seqlens;
+    int N;
+    kda_dtype act_dtype, gate_dtype, out_dtype;
+    const void *q, *k, *v, *g, *beta;
+    const float* S0;
+    void* o;
+    float* S_T;
+    void* workspace;
+    size_t workspace_bytes;
+    unsigned flags;
+} kda_chunk_args;
+
+#define KDA_FLAG_GENERIC 1u
+
+/* Arguments of kda_decode_step: one token for each of N independent sequences.
+ *   q, k, g [N, H, dk];  v [N, H, dv];  beta [N, H]   (act_dtype / gate_dtype as above)
+ *   S       [N, H, dk, dv] fp32, read and updated in place.
+ *   o       [N, H, dv] out_dtype, the output of the new token (read after the update).
+ */
+typedef struct {
+    int N, H, dk, dv;
+    kda_dtype act_dtype, gate_dtype, out_dtype;
+    const void *q, *k, *v, *g, *beta;
+    float* S;
+    void* o;
+} kda_decode_args;
+
+/* Bytes of device workspace kda_chunk_fwd needs for these arguments (pointers are not
+ * inspected). Writes 0 to *bytes when the chosen path needs none. Validates shapes and
+ * dtypes like kda_chunk_fwd. */
+kda_status kda_chunk_fwd_workspace(const kda_chunk_args* args, size_t* bytes);
+
+/* Prefill: o and S_T from q, k, v, g, beta and S0, enqueued on hip_stream (hipStream_t). */
+kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
+
+/* Decode: one step for every (sequence, head); S updated in place, o written. */
+kda_status kda_decode_step(const kda_decode_args* args, void* hip_stream);
+
+/* Device check of the preconditions on the gates: counts g values outside [-5, 0] and
+ * beta values outside [0, 1] (NaN counts as outside). n_g, n_beta elements; dtype of both
+ * is gate_dtype. Synchronises hip_stream; *n_bad receives the count. */
+kda_status kda_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
+                           kda_dtype gate_dtype, void* hip_stream, int64_t* n_bad);
+
+const char* kda_status_string(kda_status s);
+const char* kda_last_error(void);   /* detail of the last failure on this thread */
+int kda_abi_version(void);           /* KDA_ABI_VERSION of the built library */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,90 @@
+"""kda_decode_step on the GPU against the CPU oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_59_amd import inputs
+from tests.gpu_util import TAU, assert_parity, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_case(seed, N, H, dk, dv, dtype):
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta = inputs.draw_activations(rng, N, 1, H, dk, dv, dtype)
+    S = inputs.draw_state(rng, N, H, dk, dv, std=0.5)
+    return q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 32), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_decode_small(dk, dv, dtype, out_bf16):
+    import torch
+    from gated_delta_rule_59_amd import binding
+    print(f"decode small dk={dk} dv={dv} {dtype} out_bf16={out_bf16}", flush=True)
+    q, k, v, g, beta, S = decode_case(1, 7, 3, dk, dv, dtype)
+    o_ref, s_ref = oracle.kda_decode_reference(q, k, v, g, beta, S)
+    Sd = torch.from_numpy(S).cuda()
+    o = binding.decode_step(*(dev(a, dtype) for a in (q, k, v, g, beta)), Sd,
+                            out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    # fp32 arithmetic on the device: the fp32 bar holds for o (before output rounding) and S
+    assert_parity(host(Sd), s_ref, TAU["f32"], "S")
+    if out_bf16:   # rounding to bf16 costs at most 2^-8 of each value
+        bound = 2.0 ** -8 * np.abs(o_ref) + TAU["f32"] * np.sqrt(np.mean(o_ref ** 2))
+        assert (np.abs(host(o) - o_ref) <= bound).all()
+    else:
+        assert_parity(host(o), o_ref, TAU["f32"], "o")
+
+
+def test_decode_rejects_bad_args():
+    import torch
+    from gated_delta_rule_59_amd import binding
+    q, k, v, g, beta, S = decode_case(2, 2, 2, 32, 32, "f32")
+    t = [dev(a, "f32") for a in (q, k, v, g, beta)]
+    Sd = torch.from_numpy(S).cuda()
+    with pytest.raises(binding.KDAError) as e:   # o aliasing S
+        binding.decode_step(*t, Sd, o=Sd.view(-1)[: 2 * 2 * 32].view(2, 2, 32))
+    assert e.value.status == 8
+
+
+def _sampled(arrs, chains):
+    """Pack the sampled (n, h) chains as independent one-head sequences."""
+    return [np.ascontiguousarray(np.stack([a[n, h] for n, h in chains])[:, None]) for a in arrs]
+
+
+def test_decode_workload_1000_steps_sampled():
+    """The decode workload at full size: N=512, H=32, dk=dv=128, fp32 state of 1 GiB updated
+    in place for 1000 steps. o is checked at steps 1-10, 100 and 1000 and the state at step
+    1000, on 64 sampled (sequence, head) chains that the oracle follows step by step."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    N, H, dk, dv, steps = 512, 32, 128, 128, 1000
+    print("decode workload: generating state and step inputs", flush=True)
+    S_host = inputs.make_decode_state(N, H, dk, dv)
+    pool = [inputs.make_decode_step(p, N, H, dk, dv) for p in range(inputs.DECODE_POOL)]
+    pool_dev = [[dev(a, "bf16") for a in step] for step in pool]
+    rng = np.random.default_rng(123)
+    chains = sorted({(int(a), int(b)) for a, b in zip(rng.integers(0, N, 64), rng.integers(0, H, 64))})
+    chains[:2] = [(0, 0), (N - 1, H - 1)]
+    s_ref = np.stack([S_host[n, h] for n, h in chains])[:, None].astype(np.float64)
+    S = torch.from_numpy(S_host).cuda()
+    del S_host
+    o = torch.empty((N, H, dv), dtype=torch.float32, device="cuda")
+    check = set(range(1, 11)) | {100, 1000}
+    for s in range(1, steps + 1):
+        p = (s - 1) % inputs.DECODE_POOL
+        binding.decode_step(*pool_dev[p], S, o=o)
+        q, k, v, g, beta = _sampled(pool[p], chains)
+        o_ref, s_ref = oracle.kda_decode_reference(q, k, v, g, beta, s_ref)
+        if s in check:
+            torch.cuda.synchronize()
+            oh = o.cpu().numpy()
+            got = np.stack([oh[n, h] for n, h in chains])[:, None]
+            assert_parity(got, o_ref, TAU["bf16"], f"o step {s}")
+    torch.cuda.synchronize()
+    idx_n = torch.tensor([n for n, _ in chains], device="cuda")
+    idx_h = torch.tensor([h for _, h in chains], device="cuda")
+    got_s = S[idx_n, idx_h].cpu().numpy()[:, None]
+    assert_parity(got_s, s_ref, TAU["bf16"], "S step 1000")

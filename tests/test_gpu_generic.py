@@ -1,0 +1,111 @@
+"""The fp32 vector-ALU chunk path on the GPU against the oracle, and host-side behaviour
+of kda_chunk_fwd that needs a device (in-place state, determinism, gate checks)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_59_amd import inputs
+from tests.gpu_util import TAU, assert_parity, dev, host, kda_inputs_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(x, chunk, generic, out_bf16=False):
+    import torch
+    from gated_delta_rule_59_amd import binding
+    q, k, v, g, beta, S0, cu = kda_inputs_dev(x)
+    o, S_T = binding.chunk_fwd(q, k, v, g, beta, S0, cu, chunk=chunk, generic=generic,
+                               out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    return host(o), host(S_T)
+
+
+def test_tiny_f32_workload():
+    """Workload tiny-f32 (B=1, H=2, T=64, dk=dv=32, chunk 16, fp32) at the fp32 bar."""
+    x = inputs.make_prefill(0)
+    o_ref, s_ref = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0)
+    o, s = run(x, 16, generic=False)
+    assert_parity(o, o_ref, TAU["f32"], "o")
+    assert_parity(s, s_ref, TAU["f32"], "S_T")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_generic_bf16_chunk_sizes(chunk):
+    x = inputs.make_prefill(1, T=200, H=2)
+    o_ref, s_ref = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0)
+    o, s = run(x, chunk, generic=True)
+    # fp32 arithmetic: well inside the bf16 bar
+    assert_parity(o, o_ref, 1e-4, "o")
+    assert_parity(s, s_ref, 1e-4, "S_T")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (64, 128), (128, 32)])
+def test_generic_f32_head_dims(dk, dv):
+    rng = np.random.default_rng(dk * 1000 + dv)
+    q, k, v, g, beta = inputs.draw_activations(rng, 2, 70, 3, dk, dv, "f32")
+    S0 = inputs.draw_state(rng, 2, 3, dk, dv, std=0.1)
+    x = inputs.KDAInputs(inputs.Workload("t", 0, 3, dk, dv, 32, "f32", B=2, T=70), q, k, v, g,
+                         beta, S0)
+    o_ref, s_ref = oracle.kda_reference(q, k, v, g, beta, S0)
+    o, s = run(x, 32, generic=False)
+    assert_parity(o, o_ref, TAU["f32"], "o")
+    assert_parity(s, s_ref, TAU["f32"], "S_T")
+
+
+def ragged_case(dtype="bf16", H=2, d=128):
+    """Packed sequences with the edge lengths: empty, one token, a tile short of / exactly /
+    one past a chunk, and two chunks plus a partial tile."""
+    lens = [0, 1, 63, 64, 65, 137, 16]
+    rng = np.random.default_rng(77)
+    T = sum(lens)
+    q, k, v, g, beta = inputs.draw_activations(rng, 1, T, H, d, d, dtype)
+    S0 = inputs.draw_state(rng, len(lens), H, d, d)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    wl = inputs.Workload("ragged", 3, H, d, d, 64, dtype, B=1, T=T, lengths=lens, n_seq=len(lens))
+    return inputs.KDAInputs(wl, q, k, v, g, beta, S0, cu)
+
+
+def test_generic_ragged_varlen():
+    x = ragged_case()
+    o_ref, s_ref = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0, cu_seqlens=x.cu_seqlens)
+    o, s = run(x, 64, generic=True)
+    assert_parity(o, o_ref, 1e-4, "o")
+    assert_parity(s, s_ref, 1e-4, "S_T")
+    np.testing.assert_array_equal(s[0], x.S0[0])   # the empty sequence keeps its state
+
+
+def test_inplace_state_and_determinism():
+    import torch
+    from gated_delta_rule_59_amd import binding
+    x = inputs.make_prefill(1, T=130, H=2)
+    q, k, v, g, beta, S0, _ = kda_inputs_dev(x)
+    o1, s1 = binding.chunk_fwd(q, k, v, g, beta, S0, chunk=64)
+    o2, s2 = binding.chunk_fwd(q, k, v, g, beta, S0, chunk=64)
+    S = S0.clone()
+    o3, s3 = binding.chunk_fwd(q, k, v, g, beta, S, chunk=64, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, S)
+
+
+def test_gate_check_and_env_switch():
+    import torch
+    from gated_delta_rule_59_amd import binding
+    x = inputs.make_prefill(1, T=64, H=2)
+    q, k, v, g, beta, S0, _ = kda_inputs_dev(x)
+    assert binding.check_gates(g, beta) == 0
+    g2 = g.clone()
+    g2.view(-1)[:3] = -5.5
+    b2 = beta.clone()
+    b2.view(-1)[5] = 1.5
+    assert binding.check_gates(g2, b2) == 4
+    os.environ["KDA_CHECK"] = "1"
+    try:
+        binding.chunk_fwd(q, k, v, g, beta, S0)   # passes the check
+        with pytest.raises(binding.KDAError) as e:
+            binding.chunk_fwd(q, k, v, g2, beta, S0)
+        assert e.value.status == 5
+    finally:
+        del os.environ["KDA_CHECK"]
