@@ -18,7 +18,11 @@ Kimi K3 architecture page for the -5 floor on the per-step log-decay):
 
 Every array is produced in float32 and then rounded to the storage dtype; the
 float32 arrays returned hold exactly the values the kernels receive.
-Draw order per workload: (lengths) -> q -> k -> v -> beta -> g -> S0 -> (channel mask).
+Seeding: tensor X of workload w is drawn in blocks of 1024 tokens (states: 64
+(sequence, head) pairs), block i from numpy.random.default_rng([0, w, X, i]) with
+X = 1 q, 2 k, 3 v, 4 beta, 5 g, 6 S0; the varlen lengths from default_rng([0, w, 0]) and the
+pinned-channel mask from default_rng([0, w, 7]). Decode step-input set p uses the prefix
+[0, 4, 1 + p]. Blocks are independent, so they are drawn on parallel threads.
 """
 from __future__ import annotations
 
@@ -81,31 +85,63 @@ class KDAInputs:
     extra: dict = field(default_factory=dict)
 
 
-def _normal(rng, shape):
-    return rng.standard_normal(size=shape, dtype=np.float32)
+_TOK_BLOCK = 1024
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def _blocks(n, size):
+    return [(a, min(a + size, n)) for a in range(0, n, size)]
+
+
+def _draw(key, tensor, shape, transform, dtype, block=_TOK_BLOCK):
+    """float32 array of `shape`; axis 0 is cut into blocks, block i drawn from
+    default_rng([*key, tensor, i]) as N(0,1), then transform(), then rounded to dtype."""
+    out = np.empty(shape, dtype=np.float32)
+
+    def work(i_ab):
+        i, (a, b) = i_ab
+        rng = np.random.default_rng([*key, tensor, i])
+        x = rng.standard_normal(size=(b - a,) + tuple(shape[1:]), dtype=np.float32)
+        out[a:b] = to_storage(transform(x), dtype)
+
+    list(_pool().map(work, enumerate(_blocks(shape[0], block))))
+    return out
 
 
 def _unit_rows(x):
-    n = np.sqrt(np.sum(np.square(x, dtype=np.float64), axis=-1, keepdims=True))
-    return (x / n).astype(np.float32)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
 
 
 def _sigmoid(x):
-    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+    return np.float32(1.0) / (np.float32(1.0) + np.exp(-x))
 
 
-def draw_activations(rng, B, T, H, dk, dv, dtype):
-    """q, k unit rows over dk; v ~ N(0,1); beta = sigmoid(N(0,1)); g = -5 sigmoid(N(0,1))."""
-    q = to_storage(_unit_rows(_normal(rng, (B, T, H, dk))), dtype)
-    k = to_storage(_unit_rows(_normal(rng, (B, T, H, dk))), dtype)
-    v = to_storage(_normal(rng, (B, T, H, dv)), dtype)
-    beta = to_storage(_sigmoid(_normal(rng, (B, T, H))), dtype)
-    g = to_storage(GATE_FLOOR * _sigmoid(_normal(rng, (B, T, H, dk))), dtype)
+def draw_activations(key, B, T, H, dk, dv, dtype):
+    """q, k unit rows over dk; v ~ N(0,1); beta = sigmoid(N(0,1)); g = -5 sigmoid(N(0,1)).
+    Shapes [B, T, H, d] ([B, T, H] for beta); drawn over the flattened B*T token axis."""
+    n = B * T
+    q = _draw(key, 1, (n, H, dk), _unit_rows, dtype).reshape(B, T, H, dk)
+    k = _draw(key, 2, (n, H, dk), _unit_rows, dtype).reshape(B, T, H, dk)
+    v = _draw(key, 3, (n, H, dv), lambda x: x, dtype).reshape(B, T, H, dv)
+    beta = _draw(key, 4, (n, H), _sigmoid, dtype).reshape(B, T, H)
+    g = _draw(key, 5, (n, H, dk), lambda x: np.float32(GATE_FLOOR) * _sigmoid(x),
+              dtype).reshape(B, T, H, dk)
     return q, k, v, g, beta
 
 
-def draw_state(rng, n, H, dk, dv, std=0.02):
-    return (std * _normal(rng, (n, H, dk, dv))).astype(np.float32)
+def draw_state(key, n, H, dk, dv, std=0.02):
+    """fp32 states [n, H, dk, dv] ~ std * N(0,1), blocks of 64 (sequence, head) pairs."""
+    x = _draw(key, 6, (n * H, dk, dv), lambda z: np.float32(std) * z, "f32", block=64)
+    return x.reshape(n, H, dk, dv)
 
 
 WORKLOADS = {
@@ -125,11 +161,12 @@ def make_prefill(wid: int, *, T: Optional[int] = None, H: Optional[int] = None,
     wl = Workload(**{**base.__dict__})
     if H is not None:
         wl.H = H
-    rng = np.random.default_rng([0, wid])
+    key = (0, wid)
     cu = None
     if wid == 3:
         ns = n_seq if n_seq is not None else base.n_seq
         lo, hi = (512, 16384) if T is None else (max(1, T // 4), T)
+        rng = np.random.default_rng([*key, 0])
         lens = rng.integers(lo, hi, size=ns, endpoint=True).astype(np.int64)
         wl.lengths = [int(x) for x in lens]
         wl.n_seq = ns
@@ -138,12 +175,13 @@ def make_prefill(wid: int, *, T: Optional[int] = None, H: Optional[int] = None,
         cu[1:] = np.cumsum(lens)
     elif T is not None:
         wl.T = T
-    q, k, v, g, beta = draw_activations(rng, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype)
+    q, k, v, g, beta = draw_activations(key, wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.dtype)
     S0 = None
     if wid != 0:
-        S0 = draw_state(rng, wl.n_seq if wid == 3 else wl.B, wl.H, wl.dk, wl.dv)
+        S0 = draw_state(key, wl.n_seq if wid == 3 else wl.B, wl.H, wl.dk, wl.dv)
     extra = {}
     if wid == 2:
+        rng = np.random.default_rng([*key, 7])
         pinned = np.zeros((wl.H, wl.dk), dtype=bool)
         for h in range(wl.H):
             pinned[h, rng.permutation(wl.dk)[: wl.dk // 2]] = True
@@ -154,13 +192,11 @@ def make_prefill(wid: int, *, T: Optional[int] = None, H: Optional[int] = None,
 
 def make_decode_state(N: int = 512, H: int = 32, dk: int = 128, dv: int = 128) -> np.ndarray:
     """Decode workload state: fp32 [N, H, dk, dv] ~ 0.02 N(0,1) (1 GiB at the full size)."""
-    rng = np.random.default_rng([0, 4])
-    return draw_state(rng, N, H, dk, dv)
+    return draw_state((0, 4), N, H, dk, dv)
 
 
 def make_decode_step(p: int, N: int = 512, H: int = 32, dk: int = 128, dv: int = 128):
     """Step-input set p of the decode workload: q, k, g [N, H, dk], v [N, H, dv], beta [N, H]
     in bf16 values, drawn as for prefill-4k. Step s of a run uses set s % DECODE_POOL."""
-    rng = np.random.default_rng([0, 4, 1 + p])
-    q, k, v, g, beta = draw_activations(rng, N, 1, H, dk, dv, "bf16")
+    q, k, v, g, beta = draw_activations((0, 4, 1 + p), N, 1, H, dk, dv, "bf16")
     return q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]

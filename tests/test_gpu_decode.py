@@ -10,9 +10,8 @@ pytestmark = pytest.mark.gpu
 
 
 def decode_case(seed, N, H, dk, dv, dtype):
-    rng = np.random.default_rng(seed)
-    q, k, v, g, beta = inputs.draw_activations(rng, N, 1, H, dk, dv, dtype)
-    S = inputs.draw_state(rng, N, H, dk, dv, std=0.5)
+    q, k, v, g, beta = inputs.draw_activations((9, seed), N, 1, H, dk, dv, dtype)
+    S = inputs.draw_state((9, seed), N, H, dk, dv, std=0.5)
     return q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S
 
 
