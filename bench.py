@@ -1,0 +1,231 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill-4k]
+
+A step is one kda_chunk_fwd (prefill: cumulative decay, tile products, the (I + A)
+inverse, state propagation and outputs) over one batch of the workload, inputs already
+resident on the GPU. K steps are timed between two device synchronisations; every launch
+is also bracketed by HIP events on the stream it runs on. The decode half of the metric
+(GB/s against HBM peak) is measured in the same run on the decode workload (N=512
+sequences, H=32, 1 GiB fp32 state updated in place), from its own timed loop.
+
+Prints ONE JSON line. The CPU oracle is timed on a bounded sample of the same workload
+as the reported CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
+WORKLOADS = {"prefill-4k": 1, "prefill-64k-bound": 2, "varlen-16": 3}
+
+
+def flops_per_token_head(C=64, d=128):
+    """Algorithmic flops of the chunked forward per (token, head): A and Aqk (C d each), the
+    triangular solve applied to both right-hand sides (2 C d), Aqk U' (C d), and the three
+    state products (6 d^2)."""
+    return 5 * C * d + 6 * d * d
+
+
+def bytes_per_token_head(d=128, in_bytes=2, out_bytes=4):
+    """q, k, g, v (d each) and beta read once; o written once."""
+    return 4 * d * in_bytes + in_bytes + d * out_bytes
+
+
+def src_hash(*paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(profile_name, kernel_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_src_sha") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn() warmup times, then `steps` times with an event pair around each launch.
+    Returns (wall seconds for the timed steps, list of per-launch ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(x, budget_s=10.0):
+    """The oracle (fp64, as committed) on the host cores: whole passes over the workload
+    until budget_s has elapsed (at least one)."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or (os.cpu_count() or 1)
+    chains = x.wl.n_seq * x.wl.H
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0, cu_seqlens=x.cu_seqlens,
+                             threads=threads, want_state=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    tokens = x.wl.B * x.wl.T
+    return {"value": tokens * reps / el, "unit": "tokens/s", "cores": min(threads, chains),
+            "kind": "oracle",
+            "sample": f"{reps} full pass(es) of {x.wl.name} (fp64 oracle, {chains} independent "
+                      f"(sequence, head) chains over {threads} OpenMP threads), {el:.1f} s"}
+
+
+def bench_decode(steps, warmup, stream):
+    import torch
+    from gated_delta_rule_59_amd import binding, inputs
+    N, H, d = 512, 32, 128
+    S = torch.from_numpy(inputs.make_decode_state(N, H, d, d)).cuda()
+    pool = [[torch.from_numpy(a).cuda().to(torch.bfloat16) for a in inputs.make_decode_step(p)]
+            for p in range(inputs.DECODE_POOL)]
+    o = torch.empty((N, H, d), dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def step():
+        binding.decode_step(*pool[it[0] % inputs.DECODE_POOL], S, o=o, stream=stream)
+        it[0] += 1
+
+    wall, ms = time_launches(step, steps, warmup, stream)
+    per = sum(ms) / len(ms)
+    nbytes = N * H * (2 * 4 * d * d + 2 * (4 * d + 1) + 4 * d)  # state in+out, inputs, fp32 o
+    ksrc = os.path.join(ROOT, "gated_delta_rule_59_amd", "csrc", "kda_decode.hip")
+    traffic = read_traffic("decode-512_decode_step_kernel_traffic.txt", src_hash(ksrc))
+    gbs = nbytes / (per * 1e-3) / 1e9
+    return {"workload": "decode-512 (N=512, H=32, dk=dv=128, fp32 state 1 GiB, bf16 inputs, "
+                        "fp32 o)",
+            "steps": steps, "warmup": warmup, "ms_per_step": per,
+            "wall_ms_per_step": wall * 1e3 / steps,
+            "tokens_per_s": N / (per * 1e-3), "GB_per_s": gbs,
+            "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill-4k", choices=list(WORKLOADS))
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device copies of BYTES bytes (scales HBM counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); KDA "
+              "prefill and decode shard over independent (sequence, head) pairs with no "
+              "communication, so N GPUs would each run this same single-GPU workload.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "launches": 5}), flush=True)
+        return
+    from gated_delta_rule_59_amd import binding, inputs
+    binding.lib()
+    wid = WORKLOADS[args.workload]
+    x = inputs.make_prefill(wid)
+    stream = torch.cuda.current_stream()
+    dv = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)  # noqa: E731
+    q, k, v, g, beta = (dv(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    S0 = torch.from_numpy(x.S0).cuda()
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens).cuda()
+    B, T, H, d = x.q.shape
+    n_seq = x.wl.n_seq if cu is not None else B
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device="cuda")
+    S_T = torch.empty((n_seq, H, d, d), dtype=torch.float32, device="cuda")
+    nbytes_ws = binding.chunk_fwd_workspace_bytes(q, k, v, g, beta, S0, cu)
+    ws = binding.alloc_workspace(nbytes_ws, q.device)
+
+    def step():
+        binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T, workspace=ws, stream=stream)
+
+    wall, ms = time_launches(step, args.steps, args.warmup, stream)
+    per_ms = sum(ms) / len(ms)
+    token_heads = B * T * H
+    flops = flops_per_token_head() * token_heads
+    nbytes = bytes_per_token_head() * token_heads + 2 * 4 * d * d * n_seq * H
+    gbs = nbytes / (per_ms * 1e-3) / 1e9
+    tflops = flops / (per_ms * 1e-3) / 1e12
+    ksrc = [os.path.join(ROOT, "gated_delta_rule_59_amd", "csrc", f)
+            for f in ("kda_fast.hip", "kda_device.h")]
+    traffic = read_traffic(f"{args.workload}_chunk_fwd_traffic.txt", src_hash(*ksrc))
+    tokens = B * T
+    # the roofline ceiling for this path: min(matrix peak, HBM peak x flops per byte)
+    attainable = min(MFMA_PEAK_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9 * flops / nbytes)
+    res = {
+        "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode GB/s % HBM peak (1 GPU)",
+        "value": tokens / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": x.wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d,
+                   "chunk": 64, "n_seq": n_seq, "inputs": "bf16 q/k/v/g/beta",
+                   "state": "fp32", "output": "fp32", "global_batch": B, "seq_len": T},
+        "prefill": {"event_ms_per_launch": per_ms, "tokens_per_s_event": tokens / (per_ms * 1e-3),
+                    "alg_tflops": tflops, "alg_mfma_frac": tflops / MFMA_PEAK_TFLOPS,
+                    "alg_GB_per_s": gbs, "alg_hbm_frac": gbs / HBM_PEAK_GBS,
+                    "attainable_frac": (flops / (per_ms * 1e-3)) / attainable,
+                    "workspace_bytes": nbytes_ws},
+        "roofline": {"kernel": "kda_chunk_fwd launch (prep_kernel + rec_kernel)", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
+    }
+    if not args.no_decode:
+        res["decode"] = bench_decode(args.decode_steps, max(3, args.warmup // 4), stream)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -226,33 +226,39 @@ __global__ __launch_bounds__(256) void prep_kernel(
   const int t = threadIdx.x;
   // ---- load k, q (bf16) and g (fp32) rows; rows past the end are zero
   {
+    // rows past the end are read at the last valid row, then zeroed (branch-free loads)
     const int r = t >> 2, cb = t & 3;
     const bool ok = r < Cn;
-    const int64_t e = ((tok0 + r) * H + h) * DK + cb * 32;
+    const int64_t e = ((tok0 + min(r, Cn - 1)) * H + h) * DK + cb * 32;
+    u16x8 kv[4], qv[4], gv[4];
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv) {
-      u16x8 kv = {0, 0, 0, 0, 0, 0, 0, 0}, qv = kv, gv = kv;
-      if (ok) {
-        kv = *reinterpret_cast<const u16x8*>(k + e + 8 * vv);
-        qv = *reinterpret_cast<const u16x8*>(q + e + 8 * vv);
-        gv = *reinterpret_cast<const u16x8*>(g + e + 8 * vv);
-      }
+      kv[vv] = *reinterpret_cast<const u16x8*>(k + e + 8 * vv);
+      qv[vv] = *reinterpret_cast<const u16x8*>(q + e + 8 * vv);
+      gv[vv] = *reinterpret_cast<const u16x8*>(g + e + 8 * vv);
+    }
+    const uint16_t braw = beta[(tok0 + min(t & (C - 1), Cn - 1)) * H + h];
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = cb * 32 + 8 * vv + i;
-        Ks[r * KS + c] = kv[i];
-        Qs[r * KS + c] = qv[i];
-        Gs[r * GS + c] = bf16_bits_to_f32(gv[i]);
+        Ks[r * KS + c] = ok ? kv[vv][i] : (uint16_t)0;
+        Qs[r * KS + c] = ok ? qv[vv][i] : (uint16_t)0;
+        Gs[r * GS + c] = ok ? bf16_bits_to_f32(gv[vv][i]) : 0.f;
       }
-    }
-    if (t < C) Bs[t] = (t < Cn) ? bf16_bits_to_f32(beta[(tok0 + t) * H + h]) : 0.f;
+    if (t < C) Bs[t] = (t < Cn) ? bf16_bits_to_f32(braw) : 0.f;
   }
   __syncthreads();
   // ---- cumulative log-decay down the chunk, stored in log2 units
   if (t < DK) {
+    float col[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) col[r] = Gs[r * GS + t];
     float acc = 0.f;
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      acc += Gs[r * GS + t];
+      acc += col[r];
       Gs[r * GS + t] = acc * kLog2e;
     }
   }
@@ -388,8 +394,12 @@ __global__ __launch_bounds__(256) void rec_kernel(
     const uint16_t* __restrict__ v, const float* __restrict__ S0, TOut* __restrict__ o,
     float* __restrict__ S_T, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     int T, int H, int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
-  // partial sums exchanged once per chunk: [buffer][X | QS][wave][row][column]
-  __shared__ __align__(16) float xch[2][2][4][C][16];
+  // Partial sums exchanged once per chunk: [buffer][X | QS][wave][column][row]. Column-major
+  // so that the four rows a lane holds in a D tile, and the eight rows it needs for a B
+  // operand, are contiguous (16-byte LDS accesses); rows padded to 68 floats so that the 16
+  // columns of one access fall in distinct banks.
+  constexpr int XR = C + 4;
+  __shared__ __align__(16) float xch[2][2][4][16][XR];
 
   // XCD-aware placement: the 8 strips of one (sequence, head) share an XCD and its L2.
   const int b = blockIdx.x;
@@ -448,13 +458,26 @@ __global__ __launch_bounds__(256) void rec_kernel(
       for (int i = 0; i < 4; ++i) gam[u][i] = gp[32 * w + 16 * u + 4 * gq + i];
     }
   };
-  auto load_v = [&](int64_t c) {  // wave 0 only: V rows of the chunk, its D-tile layout
+  // V rows of the chunk in the D-tile layout (only wave 0's copy is used). Rows past the
+  // end are read at the last valid row and zeroed afterwards: no load sits under a branch,
+  // so the compiler can wait for exactly the loads it needs.
+  uint16_t vraw[4][4];
+  auto load_v = [&](int64_t c) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = min(c * C + 16 * mt + 4 * gq + i, si.len - 1);
+        vraw[mt][i] = v[((si.tok0 + row) * H + h) * DV + col];
+      }
+  };
+  auto take_v = [&](int64_t c) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t row = c * C + 16 * mt + 4 * gq + i;
-        vv[mt][i] = row < si.len ? bfv(v + ((si.tok0 + row) * H + h) * DV + col) : 0.f;
+        vv[mt][i] = (w == 0 && row < si.len) ? bf16_bits_to_f32(vraw[mt][i]) : 0.f;
       }
   };
   auto block = [&](int64_t c) { return ws + ((size_t)(si.cid0 + c) * H + h) * kBlockBytes; };
@@ -465,12 +488,14 @@ __global__ __launch_bounds__(256) void rec_kernel(
     load_m(b0);
     load_a(b0);
     load_kt(b0);
-    if (w == 0) load_v(0);
+    load_v(0);
   }
   int buf = 0;
   for (int64_t c = 0; c < nc; ++c) {
-    const bool more = c + 1 < nc;
-    const uint8_t* bn = more ? block(c + 1) : nullptr;
+    // operands of the next chunk are loaded right after their use in this one (the last
+    // chunk reloads itself), unconditionally, so every load has a chunk's time to land
+    const int64_t cn = min(c + 1, nc - 1);
+    const uint8_t* bn = block(cn);
     // -- partial Kbar S and Qbar S over this wave's 32 key rows
     half8 bs;
 #pragma unroll
@@ -481,35 +506,42 @@ __global__ __launch_bounds__(256) void rec_kernel(
       X[mt] = mfma_f16(kb[mt], bs, zero);
       QS[mt] = mfma_f16(qb[mt], bs, zero);
     }
-    if (more) load_kq(bn);
+    load_kq(bn);
+    take_v(c);
+    load_v(cn);
     // -- exchange: wave 0 contributes V - X_0, the others -X_w; QS parts as they are
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      floatx4 xo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * gq + i;
-        xch[buf][0][w][r][nn] = (w == 0 ? vv[mt][i] : 0.f) - X[mt][i];
-        xch[buf][1][w][r][nn] = QS[mt][i];
-      }
-    if (w == 0 && more) load_v(c + 1);
+      for (int i = 0; i < 4; ++i) xo[i] = vv[mt][i] - X[mt][i];
+      *reinterpret_cast<floatx4*>(&xch[buf][0][w][nn][16 * mt + 4 * gq]) = xo;
+      *reinterpret_cast<floatx4*>(&xch[buf][1][w][nn][16 * mt + 4 * gq]) = QS[mt];
+    }
     __syncthreads();
     // -- U' = M (V - Kbar S), all 64 rows (each wave keeps a full copy)
     half8 by[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      floatx4 lo = zero, hi = zero;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 32 * ks + kslot(gq, i);
-        by[ks][i] = static_cast<_Float16>(xch[buf][0][0][r][nn] + xch[buf][0][1][r][nn] +
-                                          xch[buf][0][2][r][nn] + xch[buf][0][3][r][nn]);
+      for (int ww = 0; ww < 4; ++ww) {
+        lo += *reinterpret_cast<const floatx4*>(&xch[buf][0][ww][nn][32 * ks + 4 * gq]);
+        hi += *reinterpret_cast<const floatx4*>(&xch[buf][0][ww][nn][32 * ks + 16 + 4 * gq]);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        by[ks][i] = static_cast<_Float16>(lo[i]);
+        by[ks][i + 4] = static_cast<_Float16>(hi[i]);
+      }
+    }
     floatx4 U[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       U[mt] = mfma_f16(mf[mt][0], by[0], zero);
       U[mt] = mfma_f16(mf[mt][1], by[1], U[mt]);
     }
-    if (more) load_m(bn);
+    load_m(bn);
     half8 uh[2], ul[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -521,13 +553,10 @@ __global__ __launch_bounds__(256) void rec_kernel(
         ul[ks][i] = ll;
       }
     // -- outputs: rows 16w .. 16w+15 of the chunk
-    floatx4 acc;
+    floatx4 acc = zero;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * gq + i;
-      acc[i] = xch[buf][1][0][r][nn] + xch[buf][1][1][r][nn] + xch[buf][1][2][r][nn] +
-               xch[buf][1][3][r][nn];
-    }
+    for (int ww = 0; ww < 4; ++ww)
+      acc += *reinterpret_cast<const floatx4*>(&xch[buf][1][ww][nn][16 * w + 4 * gq]);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (ks == 1 && w < 2) break;  // Aqk is lower triangular: rows < 32 see k-step 0 only
@@ -535,7 +564,7 @@ __global__ __launch_bounds__(256) void rec_kernel(
       acc = mfma_f16(ahi[ks], ul[ks], acc);
       acc = mfma_f16(alo[ks], uh[ks], acc);
     }
-    if (more) load_a(bn);
+    load_a(bn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = c * C + 16 * w + 4 * gq + i;
@@ -552,7 +581,7 @@ __global__ __launch_bounds__(256) void rec_kernel(
         s[u] = mfma_f16(kt[u][ks], ul[ks], s[u]);
       }
     }
-    if (more) load_kt(bn);
+    load_kt(bn);
     buf ^= 1;
   }
   if (S_T) {
