@@ -22,9 +22,10 @@
 //    are <= 1 and use fp16 (11-bit significand) directly.
 //  rec_kernel (one workgroup per sequence, head and 16 value columns, serial over chunks):
 //    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence;
-//    four waves split the 128 key rows. Per chunk: partial Kbar S and Qbar S per wave, one
-//    LDS exchange to sum them, U' = M (V - Kbar S), the outputs Qbar S + Aqk U' (Aqk and U'
-//    split into fp16 hi + lo), and the state update. Columns of S evolve independently
+//    four waves split the 128 key rows. Per chunk: the state strip is all-gathered in
+//    fp16 through LDS, each wave forms complete Kbar S and Qbar S for its own 16 chunk rows,
+//    Y = V - Kbar S is all-gathered, U' = M Y, then the outputs Qbar S + Aqk U' (Aqk and U'
+//    split into fp16 hi + lo) and the wave's rows of the state update. Columns of S evolve independently
 //    (the transition acts on the key side only), so splitting the value columns over
 //    workgroups is exact and needs no communication.
 #include "kda_device.h"
@@ -41,7 +42,7 @@ constexpr int NSTRIP = DV / 16;  // 16-column strips per (sequence, head)
 
 // Workspace block of one (chunk, head), byte offsets. Fragment f of a group starts at
 // group + f * 1024; lane l's eight fp16 values at + l * 16.
-constexpr int OFF_KB = 0;        // Kbar as A operand: [k-step over dk (4)][row tile (4)]
+constexpr int OFF_KB = 0;        // -Kbar as A operand: [k-step over dk (4)][row tile (4)]
 constexpr int OFF_QB = 16384;    // Qbar, same order
 constexpr int OFF_KT = 32768;    // Ktil^T: [dk tile (8)][k-step over chunk rows (2)]
 constexpr int OFF_M = 49152;     // M: [row tile (4)][k-step (2)]
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     for (int i = 0; i < 8; ++i) {
       const int c = 32 * ks + kslot(gq, i);
       const float e = exp2f(Gs[row * GS + c]);
-      kb[i] = static_cast<_Float16>(bfv(Ks + row * KS + c) * e);
+      kb[i] = static_cast<_Float16>(-bfv(Ks + row * KS + c) * e);
       qb[i] = static_cast<_Float16>(bfv(Qs + row * KS + c) * e);
     }
     *reinterpret_cast<half8*>(blk + OFF_KB + f * 1024 + l * 16) = kb;
@@ -385,8 +386,17 @@ __global__ __launch_bounds__(256) void prep_kernel(
 }
 
 // ---------------------------------------------------------------- rec
-__device__ __forceinline__ half8 frag(const uint8_t* blk, int off, int f, int l) {
-  return *reinterpret_cast<const half8*>(blk + off + f * 1024 + l * 16);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zero and stores
+// past the end are dropped, which is how partial chunks are masked without branches.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
+  return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
 
 template <typename TOut>
@@ -394,12 +404,14 @@ __global__ __launch_bounds__(256) void rec_kernel(
     const uint16_t* __restrict__ v, const float* __restrict__ S0, TOut* __restrict__ o,
     float* __restrict__ S_T, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     int T, int H, int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
-  // Partial sums exchanged once per chunk: [buffer][X | QS][wave][column][row]. Column-major
-  // so that the four rows a lane holds in a D tile, and the eight rows it needs for a B
-  // operand, are contiguous (16-byte LDS accesses); rows padded to 68 floats so that the 16
-  // columns of one access fall in distinct banks.
-  constexpr int XR = C + 4;
-  __shared__ __align__(16) float xch[2][2][4][16][XR];
+  // Two fp16 exchanges per chunk, double-buffered: the state strip (all 128 key rows) so
+  // every wave can form complete Kbar S and Qbar S for its own 16 chunk rows, and
+  // Y = V - Kbar S (all 64 chunk rows) for U' = M Y. Both are stored column-major
+  // ([column][row]) so that the rows a lane needs for a B operand are contiguous, with
+  // rows padded by 8 halves against bank conflicts.
+  constexpr int SR = DK + 8, YR = C + 8;
+  __shared__ __align__(16) _Float16 sx[2][16][SR];
+  __shared__ __align__(16) _Float16 yx[2][16][YR];
 
   // XCD-aware placement: the 8 strips of one (sequence, head) share an XCD and its L2.
   const int b = blockIdx.x;
@@ -412,11 +424,14 @@ __global__ __launch_bounds__(256) void rec_kernel(
   // a malformed cu_seqlens cannot make the chunk walk leave the workspace
   const int64_t nc = max((int64_t)0, min((si.len + C - 1) / C, max_chunks - si.cid0));
 
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, gq = l >> 4, nn = l & 15;
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l = t & 63, gq = l >> 4, nn = l & 15;
   const int col = 16 * strip + nn;
   const int64_t s_base = pair * DK * DV;
+  const int row_stride = H * DV;  // elements between consecutive tokens
 
-  // state rows 32w + 16u + 4gq + i (u = 0, 1), column col
+  // this wave's state rows 32w + 16u + 4gq + i (u = 0, 1), column col
   floatx4 s[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -424,70 +439,73 @@ __global__ __launch_bounds__(256) void rec_kernel(
     for (int i = 0; i < 4; ++i)
       s[u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col] : 0.f;
 
-  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-  half8 kb[4], qb[4], mf[4][2], ahi[2], alo[2], kt[2][2];
-  float gam[2][4];
-  float vv[4][4];
-  auto load_kq = [&](const uint8_t* blk) {
+  // per-lane byte offsets, fixed for the whole sequence
+  const int frag_off = l * 16;
+  int v_off[4], o_off[4];  // this wave's chunk rows 16w + 4gq + i
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      kb[mt] = frag(blk, OFF_KB, w * 4 + mt, l);
-      qb[mt] = frag(blk, OFF_QB, w * 4 + mt, l);
+  for (int i = 0; i < 4; ++i) {
+    v_off[i] = ((16 * w + 4 * gq + i) * row_stride + col) * 2;
+    o_off[i] = ((16 * w + 4 * gq + i) * row_stride + col) * (int)sizeof(TOut);
+  }
+  const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
+
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  half8 kn[4], qb[4], mf[4][2], ahi[2], alo[2], kt[2][2];
+  floatx4 gam[2];
+  uint16_t vraw[4];
+
+  // buffer bases advance by a fixed stride per chunk
+  const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * kBlockBytes;
+  const size_t blk_step = (size_t)H * kBlockBytes;
+  const uint16_t* v_base = v + (si.tok0 * H + h) * DV;
+  TOut* o_base = o + (si.tok0 * H + h) * DV;
+  const size_t tok_step = (size_t)C * row_stride;
+  // bytes of the chunk's rows of this head, up to the end of its last valid row
+  auto rows_bytes = [&](int64_t c, int elem) -> int64_t {
+    const int64_t rows = min((int64_t)C, si.len - c * C);
+    return ((rows - 1) * row_stride + DV) * elem;
+  };
+
+  auto load_kq = [&](rsrc_t r) {  // this wave's row tile, all four dk k-steps
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kn[j] = ld_frag(r, frag_off, OFF_KB + (j * 4 + w) * 1024);
+      qb[j] = ld_frag(r, frag_off, OFF_QB + (j * 4 + w) * 1024);
     }
   };
-  auto load_m = [&](const uint8_t* blk) {
+  auto load_m = [&](rsrc_t r) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) mf[mt][ks] = frag(blk, OFF_M, mt * 2 + ks, l);
+      for (int ks = 0; ks < 2; ++ks) mf[mt][ks] = ld_frag(r, frag_off, OFF_M + (mt * 2 + ks) * 1024);
   };
-  auto load_a = [&](const uint8_t* blk) {
+  auto load_a = [&](rsrc_t r) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      ahi[ks] = frag(blk, OFF_AHI, w * 2 + ks, l);
-      alo[ks] = frag(blk, OFF_ALO, w * 2 + ks, l);
+      ahi[ks] = ld_frag(r, frag_off, OFF_AHI + (w * 2 + ks) * 1024);
+      alo[ks] = ld_frag(r, frag_off, OFF_ALO + (w * 2 + ks) * 1024);
     }
   };
-  auto load_kt = [&](const uint8_t* blk) {
-    const float* gp = reinterpret_cast<const float*>(blk + OFF_GAM);
+  auto load_kt = [&](rsrc_t r) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kt[u][ks] = frag(blk, OFF_KT, (2 * w + u) * 2 + ks, l);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gam[u][i] = gp[32 * w + 16 * u + 4 * gq + i];
+      for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
+      gam[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, gam_off, 64 * u, 0));
     }
   };
-  // V rows of the chunk in the D-tile layout (only wave 0's copy is used). Rows past the
-  // end are read at the last valid row and zeroed afterwards: no load sits under a branch,
-  // so the compiler can wait for exactly the loads it needs.
-  uint16_t vraw[4][4];
   auto load_v = [&](int64_t c) {
+    const rsrc_t r = make_rsrc(v_base + c * tok_step, rows_bytes(c, 2));
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = min(c * C + 16 * mt + 4 * gq + i, si.len - 1);
-        vraw[mt][i] = v[((si.tok0 + row) * H + h) * DV + col];
-      }
+    for (int i = 0; i < 4; ++i) vraw[i] = __builtin_amdgcn_raw_buffer_load_b16(r, v_off[i], 0, 0);
   };
-  auto take_v = [&](int64_t c) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = c * C + 16 * mt + 4 * gq + i;
-        vv[mt][i] = (w == 0 && row < si.len) ? bf16_bits_to_f32(vraw[mt][i]) : 0.f;
-      }
-  };
-  auto block = [&](int64_t c) { return ws + ((size_t)(si.cid0 + c) * H + h) * kBlockBytes; };
 
   if (nc > 0) {
-    const uint8_t* b0 = block(0);
-    load_kq(b0);
-    load_m(b0);
-    load_a(b0);
-    load_kt(b0);
+    const rsrc_t r0 = make_rsrc(blk_base, (int64_t)kBlockBytes);
+    load_kq(r0);
+    load_m(r0);
+    load_a(r0);
+    load_kt(r0);
     load_v(0);
   }
   int buf = 0;
@@ -495,53 +513,62 @@ __global__ __launch_bounds__(256) void rec_kernel(
     // operands of the next chunk are loaded right after their use in this one (the last
     // chunk reloads itself), unconditionally, so every load has a chunk's time to land
     const int64_t cn = min(c + 1, nc - 1);
-    const uint8_t* bn = block(cn);
-    // -- partial Kbar S and Qbar S over this wave's 32 key rows
-    half8 bs;
+    const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+    // -- all-gather the state strip in fp16
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bs[i] = static_cast<_Float16>(i < 4 ? s[0][i] : s[1][i - 4]);
-    floatx4 X[4], QS[4];
+    for (int u = 0; u < 2; ++u) {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      half4 hv;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      X[mt] = mfma_f16(kb[mt], bs, zero);
-      QS[mt] = mfma_f16(qb[mt], bs, zero);
-    }
-    load_kq(bn);
-    take_v(c);
-    load_v(cn);
-    // -- exchange: wave 0 contributes V - X_0, the others -X_w; QS parts as they are
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      floatx4 xo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xo[i] = vv[mt][i] - X[mt][i];
-      *reinterpret_cast<floatx4*>(&xch[buf][0][w][nn][16 * mt + 4 * gq]) = xo;
-      *reinterpret_cast<floatx4*>(&xch[buf][1][w][nn][16 * mt + 4 * gq]) = QS[mt];
+      for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[u][i]);
+      *reinterpret_cast<half4*>(&sx[buf][nn][32 * w + 16 * u + 4 * gq]) = hv;
     }
     __syncthreads();
-    // -- U' = M (V - Kbar S), all 64 rows (each wave keeps a full copy)
-    half8 by[2];
+    // -- complete -Kbar S and Qbar S for this wave's 16 chunk rows
+    floatx4 X = zero, QS = zero;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      floatx4 lo = zero, hi = zero;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        lo += *reinterpret_cast<const floatx4*>(&xch[buf][0][ww][nn][32 * ks + 4 * gq]);
-        hi += *reinterpret_cast<const floatx4*>(&xch[buf][0][ww][nn][32 * ks + 16 + 4 * gq]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      half8 bs;
+      const _Float16* sp = &sx[buf][nn][32 * j + 4 * gq];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        by[ks][i] = static_cast<_Float16>(lo[i]);
-        by[ks][i + 4] = static_cast<_Float16>(hi[i]);
+        bs[i] = sp[i];
+        bs[i + 4] = sp[16 + i];
+      }
+      X = mfma_f16(kn[j], bs, X);
+      QS = mfma_f16(qb[j], bs, QS);
+    }
+    load_kq(rn);
+    // -- Y = V - Kbar S for this wave's rows, all-gathered in fp16
+    {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      half4 hy;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hy[i] = static_cast<_Float16>(X[i] + bf16_bits_to_f32(vraw[i]));
+      *reinterpret_cast<half4*>(&yx[buf][nn][16 * w + 4 * gq]) = hy;
+    }
+    load_v(cn);
+    __syncthreads();
+    // -- U' = M Y, all 64 rows (each wave keeps a full copy)
+    floatx4 U[4];
+    {
+      half8 by[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const _Float16* yp = &yx[buf][nn][32 * ks + 4 * gq];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          by[ks][i] = yp[i];
+          by[ks][i + 4] = yp[16 + i];
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        U[mt] = mfma_f16(mf[mt][0], by[0], zero);
+        U[mt] = mfma_f16(mf[mt][1], by[1], U[mt]);
       }
     }
-    floatx4 U[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      U[mt] = mfma_f16(mf[mt][0], by[0], zero);
-      U[mt] = mfma_f16(mf[mt][1], by[1], U[mt]);
-    }
-    load_m(bn);
+    load_m(rn);
     half8 uh[2], ul[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -552,11 +579,8 @@ __global__ __launch_bounds__(256) void rec_kernel(
         uh[ks][i] = hh;
         ul[ks][i] = ll;
       }
-    // -- outputs: rows 16w .. 16w+15 of the chunk
-    floatx4 acc = zero;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
-      acc += *reinterpret_cast<const floatx4*>(&xch[buf][1][ww][nn][16 * w + 4 * gq]);
+    // -- outputs of this wave's rows: Qbar S + Aqk U'
+    floatx4 acc = QS;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (ks == 1 && w < 2) break;  // Aqk is lower triangular: rows < 32 see k-step 0 only
@@ -564,24 +588,28 @@ __global__ __launch_bounds__(256) void rec_kernel(
       acc = mfma_f16(ahi[ks], ul[ks], acc);
       acc = mfma_f16(alo[ks], uh[ks], acc);
     }
-    load_a(bn);
+    load_a(rn);
+    {
+      const rsrc_t ro = make_rsrc(o_base + c * tok_step, rows_bytes(c, (int)sizeof(TOut)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = c * C + 16 * w + 4 * gq + i;
-      if (row < si.len) st(o, ((si.tok0 + row) * H + h) * DV + col, acc[i]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(TOut) == 4)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), ro, o_off[i], 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i]), ro, o_off[i], 0, 0);
+      }
     }
-    // -- state: S = Diag(e^{G_C}) S + Ktil^T U'
+    // -- this wave's state rows: S = Diag(e^{G_C}) S + Ktil^T U'
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[u][i] *= gam[u][i];
+      s[u] *= gam[u];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         s[u] = mfma_f16(kt[u][ks], uh[ks], s[u]);
         s[u] = mfma_f16(kt[u][ks], ul[ks], s[u]);
       }
     }
-    load_kt(bn);
+    load_kt(rn);
     buf ^= 1;
   }
   if (S_T) {
