@@ -51,10 +51,6 @@ constexpr int OFF_ALO = 65536;   // Aqk lo
 constexpr int OFF_GAM = 73728;   // e^{G_C}, fp32 [128]
 constexpr size_t kBlockBytes = 74240;
 
-// LDS row strides (elements), padded against bank conflicts.
-constexpr int GS = DK + 1;  // fp32 cumulative log2-decay rows
-constexpr int KS = DK + 2;  // bf16 k and q rows
-
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
   int64_t len;
@@ -112,96 +108,42 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
   if (t == 255) chunk_off[n_seq] = (int32_t)acc;
 }
 
-__device__ __forceinline__ float bfv(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+// ---------------------------------------------------------------- prep
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-// ---------------------------------------------------------------- prep: A and Aqk tiles
-// Wave `a` computes row tile a of A and Aqk: blocks (a, b) for b <= a, K = 128 in four
-// k-steps of 32 channels.
-template <int A_TILE>
-__device__ __forceinline__ void tile_products(const uint16_t* Ks, const uint16_t* Qs,
-                                              const float* Gs, int l, floatx4 (&akk)[4],
-                                              floatx4 (&aqk)[4]) {
-  const int g = l >> 4, m = l & 15;
-  const int rr = 16 * A_TILE + m;          // row operand: chunk row
-  const float* ref = Gs + (A_TILE > 0 ? 16 * A_TILE - 1 : 0) * GS;  // log2-decay before the row tile
-#pragma unroll
-  for (int b = 0; b < 4; ++b) akk[b] = aqk[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float rk[8], rq[8], refc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = 32 * ks + kslot(g, i);
-      refc[i] = A_TILE > 0 ? ref[c] : 0.f;
-      const float f = exp2f(Gs[rr * GS + c] - refc[i]);
-      rk[i] = bfv(Ks + rr * KS + c) * f;
-      rq[i] = bfv(Qs + rr * KS + c) * f;
-    }
-    half8 rk16, rq16;
-    bf16x8 rkh, rkl, rqh, rql;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      rk16[i] = static_cast<_Float16>(rk[i]);
-      rq16[i] = static_cast<_Float16>(rq[i]);
-      __bf16 h, lo;
-      split_bf16(rk[i], h, lo); rkh[i] = h; rkl[i] = lo;
-      split_bf16(rq[i], h, lo); rqh[i] = h; rql[i] = lo;
-    }
-#pragma unroll
-    for (int b = 0; b <= A_TILE; ++b) {
-      const int jj = 16 * b + m;  // column operand: chunk row j
-      float cv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = 32 * ks + kslot(g, i);
-        cv[i] = bfv(Ks + jj * KS + c) * exp2f(refc[i] - Gs[jj * GS + c]);
-      }
-      if (b < A_TILE) {  // factors <= 1: fp16
-        half8 c16;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c16[i] = static_cast<_Float16>(cv[i]);
-        akk[b] = mfma_f16(rk16, c16, akk[b]);
-        aqk[b] = mfma_f16(rq16, c16, aqk[b]);
-      } else {  // diagonal tile: column factor up to e^80, bf16 hi + lo
-        bf16x8 ch, cl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __bf16 h, lo;
-          split_bf16(cv[i], h, lo);
-          ch[i] = h;
-          cl[i] = lo;
-        }
-        akk[b] = mfma_bf16(rkh, ch, akk[b]);
-        akk[b] = mfma_bf16(rkh, cl, akk[b]);
-        akk[b] = mfma_bf16(rkl, ch, akk[b]);
-        aqk[b] = mfma_bf16(rqh, ch, aqk[b]);
-        aqk[b] = mfma_bf16(rqh, cl, aqk[b]);
-        aqk[b] = mfma_bf16(rql, ch, aqk[b]);
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void prep_kernel(
+// One workgroup per (chunk, head); wave a owns row tile a (chunk rows 16a .. 16a+15). In the
+// MFMA fragment layout lane l of wave a holds row 16a + (l & 15) and, for each of the four
+// 32-channel k-steps, the eight channels 32 ks + kslot(l >> 4, i). Every per-element quantity
+// is formed once, in registers, in that layout:
+//   rf = e^{G_r - ref_a}   (ref_a = G at the last token before tile a)   in [e^-80, 1]
+//   cf = e^{Gend_a - G_r}  (Gend_a = G at the last token of tile a)       in [e^-80, 1]
+// The row operand of tile a is k rf (q rf), its diagonal column operand k / rf (in [1, e^80]
+// times k, bf16 range), and the column operand it lends to later tiles b > a is k cf, scaled
+// there by the per-channel factor e^{ref_b - Gend_a} <= 1. Kbar, Qbar and Ktil follow from the
+// same values times per-channel constants.
+__global__ __launch_bounds__(256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
     int n_seq, uint8_t* __restrict__ ws) {
-  // Phase 1 layout: Ks, Qs (bf16 [64][KS]) then Gs (fp32 [64][GS]).
-  // Phase 2 (after the products): A32, AQ32 over Ks/Qs; T32, Xs over Gs.
-  __shared__ __align__(16) unsigned char smem[2 * 64 * KS * 2 + 64 * GS * 4];
+  constexpr int GSR = DK + 4;   // log2 cumulative decay rows (fp32)
+  constexpr int KTR = C + 8;    // Ktil^T rows (fp16, channel-major)
+  // R1: G (fp32 [64][GSR]) -> Ktil^T (fp16 [128][KTR]) -> A, Aqk (fp32 [64][64] each)
+  // R2: column operands k cf (fp32, fragment order [tile][ks][lane][8]) -> T (fp32 [64][64]), X
+  __shared__ __align__(16) float R1[64 * GSR];
+  __shared__ __align__(16) float R2[4 * 4 * 64 * 8];
+  __shared__ __align__(16) float REF2[4][DK], END2[4][DK], PCH[4][DK], ECH[4][DK], XCH[3][DK];
   __shared__ float Bs[C];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Qs = Ks + 64 * KS;
-  float* Gs = reinterpret_cast<float*>(smem + 2 * 64 * KS * 2);
-  float* A32 = reinterpret_cast<float*>(smem);  // [64][64]
-  float* AQ32 = A32 + 64 * 64;                  // [64][64]
-  float* T32 = Gs;                              // [64][64]
-  float* Xs = Gs + 64 * 64;                     // [3][16][16]
+  float* Gs = R1;
+  _Float16* KtT = reinterpret_cast<_Float16*>(R1);
+  float* A32 = R1;
+  float* AQ32 = R1 + 64 * 64;
+  float* T32 = R2;
+  float* Xs = R2 + 64 * 64;
 
   const int h = blockIdx.x % H;
   const int64_t cid = blockIdx.x / H;
-  // locate the chunk: sequence n and chunk index within it
   int n;
   int64_t c_in;
   if (cu) {
@@ -225,97 +167,198 @@ __global__ __launch_bounds__(256) void prep_kernel(
   uint8_t* blk = ws + ((size_t)cid * H + h) * kBlockBytes;
 
   const int t = threadIdx.x;
-  // ---- load k, q (bf16) and g (fp32) rows; rows past the end are zero
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l = t & 63, gq = l >> 4, m = l & 15;
+
+  // ---- phase 1: g rows into LDS (rows past the end read as 0), beta
   {
-    // rows past the end are read at the last valid row, then zeroed (branch-free loads)
     const int r = t >> 2, cb = t & 3;
     const bool ok = r < Cn;
     const int64_t e = ((tok0 + min(r, Cn - 1)) * H + h) * DK + cb * 32;
-    u16x8 kv[4], qv[4], gv[4];
+    u16x8 gv[4];
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-      kv[vv] = *reinterpret_cast<const u16x8*>(k + e + 8 * vv);
-      qv[vv] = *reinterpret_cast<const u16x8*>(q + e + 8 * vv);
-      gv[vv] = *reinterpret_cast<const u16x8*>(g + e + 8 * vv);
-    }
+    for (int vv = 0; vv < 4; ++vv) gv[vv] = *reinterpret_cast<const u16x8*>(g + e + 8 * vv);
     const uint16_t braw = beta[(tok0 + min(t & (C - 1), Cn - 1)) * H + h];
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv)
+    for (int vv = 0; vv < 4; ++vv) {
+      floatx4 lo4, hi4;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = cb * 32 + 8 * vv + i;
-        Ks[r * KS + c] = ok ? kv[vv][i] : (uint16_t)0;
-        Qs[r * KS + c] = ok ? qv[vv][i] : (uint16_t)0;
-        Gs[r * GS + c] = ok ? bf16_bits_to_f32(gv[vv][i]) : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        lo4[i] = ok ? bf16_bits_to_f32(gv[vv][i]) : 0.f;
+        hi4[i] = ok ? bf16_bits_to_f32(gv[vv][i + 4]) : 0.f;
       }
+      *reinterpret_cast<floatx4*>(&Gs[r * GSR + cb * 32 + 8 * vv]) = lo4;
+      *reinterpret_cast<floatx4*>(&Gs[r * GSR + cb * 32 + 8 * vv + 4]) = hi4;
+    }
     if (t < C) Bs[t] = (t < Cn) ? bf16_bits_to_f32(braw) : 0.f;
   }
   __syncthreads();
-  // ---- cumulative log-decay down the chunk, stored in log2 units
+  // ---- cumulative log-decay per channel (log2 units) and the per-channel constants
   if (t < DK) {
     float col[C];
 #pragma unroll
-    for (int r = 0; r < C; ++r) col[r] = Gs[r * GS + t];
+    for (int r = 0; r < C; ++r) col[r] = Gs[r * GSR + t];
     float acc = 0.f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       acc += col[r];
-      Gs[r * GS + t] = acc * kLog2e;
+      col[r] = acc * kLog2e;
+      Gs[r * GSR + t] = col[r];
+    }
+    float ref[4], end[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      ref[a] = a ? col[16 * a - 1] : 0.f;
+      end[a] = col[16 * a + 15];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      REF2[a][t] = ref[a];
+      END2[a][t] = end[a];
+      PCH[a][t] = exp2f(ref[a]);             // e^{ref_a}: Kbar = (k rf) e^{ref_a}
+      ECH[a][t] = exp2f(end[3] - end[a]);    // e^{G_C - Gend_a}: Ktil = (k cf) e^{G_C - Gend_a}
+    }
+    XCH[0][t] = exp2f(end[1] - end[0]);      // column factor of block (2, 0)
+    XCH[1][t] = exp2f(end[2] - end[0]);      // (3, 0)
+    XCH[2][t] = exp2f(end[2] - end[1]);      // (3, 1)
+    reinterpret_cast<float*>(blk + OFF_GAM)[t] = exp2f(end[3]);
+  }
+  __syncthreads();
+  // ---- phase 2: this lane's 32 elements of row 16w + m
+  const int row = 16 * w + m;
+  const bool row_ok = row < Cn;
+  const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
+  float kr[4][8], qr[4][8], kd[4][8];  // k rf, q rf, k / rf
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c0 = 32 * ks + 4 * gq;
+    u16x4 k0 = *reinterpret_cast<const u16x4*>(k + erow + c0);
+    u16x4 k1 = *reinterpret_cast<const u16x4*>(k + erow + c0 + 16);
+    u16x4 q0 = *reinterpret_cast<const u16x4*>(q + erow + c0);
+    u16x4 q1 = *reinterpret_cast<const u16x4*>(q + erow + c0 + 16);
+    const floatx4 g0 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0]);
+    const floatx4 g1 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0 + 16]);
+    const floatx4 r0 = *reinterpret_cast<const floatx4*>(&REF2[w][c0]);
+    const floatx4 r1 = *reinterpret_cast<const floatx4*>(&REF2[w][c0 + 16]);
+    const floatx4 e0 = *reinterpret_cast<const floatx4*>(&END2[w][c0]);
+    const floatx4 e1 = *reinterpret_cast<const floatx4*>(&END2[w][c0 + 16]);
+    const floatx4 p0 = *reinterpret_cast<const floatx4*>(&PCH[w][c0]);
+    const floatx4 p1 = *reinterpret_cast<const floatx4*>(&PCH[w][c0 + 16]);
+    half8 knf, qbf;
+    floatx4 kc0, kc1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = i & 3;
+      const float kv = row_ok ? bf16_bits_to_f32(i < 4 ? k0[j] : k1[j]) : 0.f;
+      const float qv = row_ok ? bf16_bits_to_f32(i < 4 ? q0[j] : q1[j]) : 0.f;
+      const float gg = i < 4 ? g0[j] : g1[j];
+      const float rf = exp2f(gg - (i < 4 ? r0[j] : r1[j]));
+      const float cf = exp2f((i < 4 ? e0[j] : e1[j]) - gg);
+      kr[ks][i] = kv * rf;
+      qr[ks][i] = qv * rf;
+      kd[ks][i] = kv * __builtin_amdgcn_rcpf(rf);
+      const float kcv = kv * cf;
+      if (i < 4) kc0[j] = kcv; else kc1[j] = kcv;
+      const float pe = i < 4 ? p0[j] : p1[j];
+      knf[i] = static_cast<_Float16>(-kr[ks][i] * pe);
+      qbf[i] = static_cast<_Float16>(qr[ks][i] * pe);
+    }
+    // Kbar (negated) and Qbar fragments [ks][row tile w]
+    *reinterpret_cast<half8*>(blk + OFF_KB + (ks * 4 + w) * 1024 + l * 16) = knf;
+    *reinterpret_cast<half8*>(blk + OFF_QB + (ks * 4 + w) * 1024 + l * 16) = qbf;
+    // column operand k cf lent to later row tiles
+    float* kcp = R2 + ((w * 4 + ks) * 64 + l) * 8;
+    *reinterpret_cast<floatx4*>(kcp) = kc0;
+    *reinterpret_cast<floatx4*>(kcp + 4) = kc1;
+  }
+  __syncthreads();  // every wave has read G: R1 is reused for Ktil^T
+  // Ktil = (k cf) e^{G_C - Gend_w}, transposed to channel-major for its fragments
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float* kcp = R2 + ((w * 4 + ks) * 64 + l) * 8;
+    const int c0 = 32 * ks + 4 * gq;
+    const floatx4 v0 = *reinterpret_cast<const floatx4*>(kcp);
+    const floatx4 v1 = *reinterpret_cast<const floatx4*>(kcp + 4);
+    const floatx4 x0 = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
+    const floatx4 x1 = *reinterpret_cast<const floatx4*>(&ECH[w][c0 + 16]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      KtT[(c0 + i) * KTR + row] = static_cast<_Float16>(v0[i] * x0[i]);
+      KtT[(c0 + 16 + i) * KTR + row] = static_cast<_Float16>(v1[i] * x1[i]);
     }
   }
   __syncthreads();
-  const int l = t & 63, gq = l >> 4, m = l & 15;
-  // ---- e^{G_C}
-  if (t < DK) reinterpret_cast<float*>(blk + OFF_GAM)[t] = exp2f(Gs[(C - 1) * GS + t]);
-  // ---- Kbar, Qbar fragments: [ks][row tile]
+  // ---- Ktil^T fragments [dk tile][ks over chunk rows]: four per wave
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = (t >> 6) + 4 * j;  // 0..15
-    const int ks = f >> 2, mt = f & 3;
-    const int row = 16 * mt + m;
-    half8 kb, qb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = 32 * ks + kslot(gq, i);
-      const float e = exp2f(Gs[row * GS + c]);
-      kb[i] = static_cast<_Float16>(-bfv(Ks + row * KS + c) * e);
-      qb[i] = static_cast<_Float16>(bfv(Qs + row * KS + c) * e);
-    }
-    *reinterpret_cast<half8*>(blk + OFF_KB + f * 1024 + l * 16) = kb;
-    *reinterpret_cast<half8*>(blk + OFF_QB + f * 1024 + l * 16) = qb;
-  }
-  // ---- Ktil^T fragments: [dk tile][ks over chunk rows]
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = (t >> 6) + 4 * j;
+  for (int jf = 0; jf < 4; ++jf) {
+    const int f = w * 4 + jf;
     const int mt = f >> 1, ks = f & 1;
-    const int ch = 16 * mt + m;
-    const float gC = Gs[(C - 1) * GS + ch];
+    const _Float16* src = KtT + (16 * mt + m) * KTR + 32 * ks + 4 * gq;
+    const half4 a0 = *reinterpret_cast<const half4*>(src);
+    const half4 a1 = *reinterpret_cast<const half4*>(src + 16);
     half8 kt;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 32 * ks + kslot(gq, i);
-      kt[i] = static_cast<_Float16>(bfv(Ks + row * KS + ch) * exp2f(gC - Gs[row * GS + ch]));
+    for (int i = 0; i < 4; ++i) {
+      kt[i] = a0[i];
+      kt[i + 4] = a1[i];
     }
     *reinterpret_cast<half8*>(blk + OFF_KT + f * 1024 + l * 16) = kt;
   }
-  // ---- A and Aqk on the matrix cores, wave w = row tile w
+  // ---- A = beta K K^T and Aqk = Q K^T tiles of row tile w on the matrix cores
   floatx4 akk[4], aqk[4];
-  const int w = t >> 6;
-  switch (w) {
-    case 0: tile_products<0>(Ks, Qs, Gs, l, akk, aqk); break;
-    case 1: tile_products<1>(Ks, Qs, Gs, l, akk, aqk); break;
-    case 2: tile_products<2>(Ks, Qs, Gs, l, akk, aqk); break;
-    default: tile_products<3>(Ks, Qs, Gs, l, akk, aqk); break;
-  }
-  __syncthreads();  // Ks, Qs, Gs are dead from here on
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int bb = 0; bb < 4; ++bb) akk[bb] = aqk[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    half8 rk16, rq16;
+    bf16x8 rkh, rkl, rqh, rql, ch, cl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      rk16[i] = static_cast<_Float16>(kr[ks][i]);
+      rq16[i] = static_cast<_Float16>(qr[ks][i]);
+      __bf16 hh, ll;
+      split_bf16(kr[ks][i], hh, ll); rkh[i] = hh; rkl[i] = ll;
+      split_bf16(qr[ks][i], hh, ll); rqh[i] = hh; rql[i] = ll;
+      split_bf16(kd[ks][i], hh, ll); ch[i] = hh; cl[i] = ll;
+    }
+    // diagonal tile: column factor up to e^80, split bf16
+    akk[w] = mfma_bf16(rkh, ch, akk[w]);
+    akk[w] = mfma_bf16(rkh, cl, akk[w]);
+    akk[w] = mfma_bf16(rkl, ch, akk[w]);
+    aqk[w] = mfma_bf16(rqh, ch, aqk[w]);
+    aqk[w] = mfma_bf16(rqh, cl, aqk[w]);
+    aqk[w] = mfma_bf16(rql, ch, aqk[w]);
+    // earlier tiles: factors <= 1, fp16
+#pragma unroll
+    for (int bb = 0; bb < 3; ++bb) {
+      if (bb >= w) break;
+      const float* kcp = R2 + ((bb * 4 + ks) * 64 + l) * 8;
+      const floatx4 c0 = *reinterpret_cast<const floatx4*>(kcp);
+      const floatx4 c1 = *reinterpret_cast<const floatx4*>(kcp + 4);
+      floatx4 x0 = {1.f, 1.f, 1.f, 1.f}, x1 = x0;
+      if (bb < w - 1) {  // blocks (2,0), (3,0), (3,1): e^{ref_w - Gend_bb}
+        const int xi = (w == 2) ? 0 : (bb == 0 ? 1 : 2);
+        x0 = *reinterpret_cast<const floatx4*>(&XCH[xi][32 * ks + 4 * gq]);
+        x1 = *reinterpret_cast<const floatx4*>(&XCH[xi][32 * ks + 16 + 4 * gq]);
+      }
+      half8 c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c16[i] = static_cast<_Float16>(c0[i] * x0[i]);
+        c16[i + 4] = static_cast<_Float16>(c1[i] * x1[i]);
+      }
+      akk[bb] = mfma_f16(rk16, c16, akk[bb]);
+      aqk[bb] = mfma_f16(rq16, c16, aqk[bb]);
+    }
+  }
+  __syncthreads();  // Ktil^T and the lent column operands are dead: R1, R2 reused
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * gq + i, jc = 16 * b + m;
-      A32[r * 64 + jc] = (b <= w && jc < r) ? Bs[r] * akk[b][i] : 0.f;
-      AQ32[r * 64 + jc] = (b <= w && jc <= r) ? aqk[b][i] : 0.f;
+      const int r = 16 * w + 4 * gq + i, jc = 16 * bb + m;
+      A32[r * 64 + jc] = (bb <= w && jc < r) ? Bs[r] * akk[bb][i] : 0.f;
+      AQ32[r * 64 + jc] = (bb <= w && jc <= r) ? aqk[bb][i] : 0.f;
     }
   }
   for (int i = t; i < 64 * 64; i += 256) T32[i] = 0.f;
@@ -326,11 +369,11 @@ __global__ __launch_bounds__(256) void prep_kernel(
     float col[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float s = 0.f;
+      float sacc = 0.f;
 #pragma unroll
       for (int mm = 0; mm < i; ++mm)
-        if (mm >= j) s += A32[(o + i) * 64 + o + mm] * col[mm];
-      col[i] = (i < j) ? 0.f : (i == j ? 1.f : -s);
+        if (mm >= j) sacc += A32[(o + i) * 64 + o + mm] * col[mm];
+      col[i] = (i < j) ? 0.f : (i == j ? 1.f : -sacc);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) T32[(o + i) * 64 + o + j] = col[i];
@@ -365,17 +408,17 @@ __global__ __launch_bounds__(256) void prep_kernel(
   }
   // ---- M = T diag(beta) and Aqk hi/lo fragments: [row tile][ks]
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int f = (t >> 6) + 4 * j;  // 0..7
+  for (int jf = 0; jf < 2; ++jf) {
+    const int f = (t >> 6) + 4 * jf;  // 0..7
     const int mt = f >> 1, ks = f & 1;
-    const int row = 16 * mt + m;
+    const int rr = 16 * mt + m;
     half8 mf, ah, al;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int cc = 32 * ks + kslot(gq, i);
-      mf[i] = static_cast<_Float16>(T32[row * 64 + cc] * Bs[cc]);
+      mf[i] = static_cast<_Float16>(T32[rr * 64 + cc] * Bs[cc]);
       _Float16 hh, ll;
-      split_f16(AQ32[row * 64 + cc], hh, ll);
+      split_f16(AQ32[rr * 64 + cc], hh, ll);
       ah[i] = hh;
       al[i] = ll;
     }
@@ -451,7 +494,7 @@ __global__ __launch_bounds__(256) void rec_kernel(
 
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
   half8 kn[4], qb[4], mf[4][2], ahi[2], alo[2], kt[2][2];
-  floatx4 gam[2];
+  floatx4 gam[2], gam_nx[2];  // e^{G_C} of the current and of the next chunk
   uint16_t vraw[4];
 
   // buffer bases advance by a fixed stride per chunk
@@ -466,12 +509,15 @@ __global__ __launch_bounds__(256) void rec_kernel(
     return ((rows - 1) * row_stride + DV) * elem;
   };
 
-  auto load_kq = [&](rsrc_t r) {  // this wave's row tile, all four dk k-steps
+  auto load_kq = [&](rsrc_t r) {  // this wave's row tile, all four dk k-steps; e^{G_C}
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kn[j] = ld_frag(r, frag_off, OFF_KB + (j * 4 + w) * 1024);
       qb[j] = ld_frag(r, frag_off, OFF_QB + (j * 4 + w) * 1024);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      gam_nx[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, gam_off, 64 * u, 0));
   };
   auto load_m = [&](rsrc_t r) {
 #pragma unroll
@@ -491,7 +537,6 @@ __global__ __launch_bounds__(256) void rec_kernel(
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
-      gam[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, gam_off, 64 * u, 0));
     }
   };
   auto load_v = [&](int64_t c) {
@@ -500,13 +545,13 @@ __global__ __launch_bounds__(256) void rec_kernel(
     for (int i = 0; i < 4; ++i) vraw[i] = __builtin_amdgcn_raw_buffer_load_b16(r, v_off[i], 0, 0);
   };
 
-  if (nc > 0) {
+  if (nc > 0) {  // same issue order as in the loop, so the loop's memory waits stay partial
     const rsrc_t r0 = make_rsrc(blk_base, (int64_t)kBlockBytes);
     load_kq(r0);
+    load_v(0);
     load_m(r0);
     load_a(r0);
     load_kt(r0);
-    load_v(0);
   }
   int buf = 0;
   for (int64_t c = 0; c < nc; ++c) {
@@ -514,6 +559,8 @@ __global__ __launch_bounds__(256) void rec_kernel(
     // chunk reloads itself), unconditionally, so every load has a chunk's time to land
     const int64_t cn = min(c + 1, nc - 1);
     const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+    gam[0] = gam_nx[0];
+    gam[1] = gam_nx[1];
     // -- all-gather the state strip in fp16
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -580,10 +627,11 @@ __global__ __launch_bounds__(256) void rec_kernel(
         ul[ks][i] = ll;
       }
     // -- outputs of this wave's rows: Qbar S + Aqk U'
+    // (for rows < 32 the second k-step multiplies the zero upper part of Aqk; it is kept
+    // so that the loop body has no branch and every memory wait stays exact)
     floatx4 acc = QS;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 1 && w < 2) break;  // Aqk is lower triangular: rows < 32 see k-step 0 only
       acc = mfma_f16(ahi[ks], uh[ks], acc);
       acc = mfma_f16(ahi[ks], ul[ks], acc);
       acc = mfma_f16(alo[ks], uh[ks], acc);
