@@ -170,6 +170,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l = t & 63, gq = l >> 4, m = l & 15;
 
+  // this lane's k and q elements (row 16w + m, fragment channels), issued first so their
+  // latency overlaps phase 1
+  const int row = 16 * w + m;
+  const bool row_ok = row < Cn;
+  u16x4 kraw[4][2], qraw[4][2];
+  {
+    const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c0 = 32 * ks + 4 * gq;
+      kraw[ks][0] = *reinterpret_cast<const u16x4*>(k + erow + c0);
+      kraw[ks][1] = *reinterpret_cast<const u16x4*>(k + erow + c0 + 16);
+      qraw[ks][0] = *reinterpret_cast<const u16x4*>(q + erow + c0);
+      qraw[ks][1] = *reinterpret_cast<const u16x4*>(q + erow + c0 + 16);
+    }
+  }
   // ---- phase 1: g rows into LDS (rows past the end read as 0), beta
   {
     const int r = t >> 2, cb = t & 3;
@@ -224,18 +240,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     reinterpret_cast<float*>(blk + OFF_GAM)[t] = exp2f(end[3]);
   }
   __syncthreads();
-  // ---- phase 2: this lane's 32 elements of row 16w + m
-  const int row = 16 * w + m;
-  const bool row_ok = row < Cn;
-  const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
+  // ---- phase 2: this lane's 32 elements of row 16w + m (k, q loaded before phase 1)
   float kr[4][8], qr[4][8], kd[4][8];  // k rf, q rf, k / rf
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int c0 = 32 * ks + 4 * gq;
-    u16x4 k0 = *reinterpret_cast<const u16x4*>(k + erow + c0);
-    u16x4 k1 = *reinterpret_cast<const u16x4*>(k + erow + c0 + 16);
-    u16x4 q0 = *reinterpret_cast<const u16x4*>(q + erow + c0);
-    u16x4 q1 = *reinterpret_cast<const u16x4*>(q + erow + c0 + 16);
+    const u16x4 k0 = kraw[ks][0], k1 = kraw[ks][1], q0 = qraw[ks][0], q1 = qraw[ks][1];
     const floatx4 g0 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0]);
     const floatx4 g1 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0 + 16]);
     const floatx4 r0 = *reinterpret_cast<const floatx4*>(&REF2[w][c0]);
@@ -442,25 +452,27 @@ __device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
 
-template <typename TOut>
+template <typename TOut, int NT>
 __global__ __launch_bounds__(256) void rec_kernel(
     const uint16_t* __restrict__ v, const float* __restrict__ S0, TOut* __restrict__ o,
     float* __restrict__ S_T, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     int T, int H, int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
-  // Two fp16 exchanges per chunk, double-buffered: the state strip (all 128 key rows) so
-  // every wave can form complete Kbar S and Qbar S for its own 16 chunk rows, and
-  // Y = V - Kbar S (all 64 chunk rows) for U' = M Y. Both are stored column-major
-  // ([column][row]) so that the rows a lane needs for a B operand are contiguous, with
-  // rows padded by 8 halves against bank conflicts.
+  // A workgroup owns NT strips of 16 value columns; every operand fragment a wave loads
+  // feeds NT matrix products. Two fp16 exchanges per chunk, double-buffered: the state
+  // strips (all 128 key rows), so every wave can form complete Kbar S and Qbar S for its own
+  // 16 chunk rows, and Y = V - Kbar S (all 64 chunk rows) for U' = M Y. Both are stored
+  // column-major ([column][row]) so the rows a lane needs for a B operand are contiguous,
+  // with rows padded by 8 halves against bank conflicts.
+  constexpr int NG = NSTRIP / NT;  // strip groups per (sequence, head)
   constexpr int SR = DK + 8, YR = C + 8;
-  __shared__ __align__(16) _Float16 sx[2][16][SR];
-  __shared__ __align__(16) _Float16 yx[2][16][YR];
+  __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];
+  __shared__ __align__(16) _Float16 yx[2][NT * 16][YR];
 
-  // XCD-aware placement: the 8 strips of one (sequence, head) share an XCD and its L2.
+  // XCD-aware placement: the strip groups of one (sequence, head) share an XCD and its L2.
   const int b = blockIdx.x;
   const int xcd = b & 7, rest = b >> 3;
-  const int strip = rest % NSTRIP;
-  const int64_t pair = (int64_t)(rest / NSTRIP) * 8 + xcd;
+  const int sg = rest % NG;
+  const int64_t pair = (int64_t)(rest / NG) * 8 + xcd;
   if (pair >= (int64_t)n_seq * H) return;
   const int n = (int)(pair / H), h = (int)(pair % H);
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
@@ -470,32 +482,38 @@ __global__ __launch_bounds__(256) void rec_kernel(
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l = t & 63, gq = l >> 4, nn = l & 15;
-  const int col = 16 * strip + nn;
   const int64_t s_base = pair * DK * DV;
   const int row_stride = H * DV;  // elements between consecutive tokens
+  int col[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) col[nt] = 16 * (NT * sg + nt) + nn;
 
-  // this wave's state rows 32w + 16u + 4gq + i (u = 0, 1), column col
-  floatx4 s[2];
+  // this wave's state rows 32w + 16u + 4gq + i (u = 0, 1), columns col[nt]
+  floatx4 s[NT][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col] : 0.f;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[nt][u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] : 0.f;
 
   // per-lane byte offsets, fixed for the whole sequence
   const int frag_off = l * 16;
-  int v_off[4], o_off[4];  // this wave's chunk rows 16w + 4gq + i
+  int v_off[NT][4], o_off[NT][4];  // this wave's chunk rows 16w + 4gq + i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v_off[i] = ((16 * w + 4 * gq + i) * row_stride + col) * 2;
-    o_off[i] = ((16 * w + 4 * gq + i) * row_stride + col) * (int)sizeof(TOut);
-  }
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + col[nt]) * 2;
+      o_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + col[nt]) * (int)sizeof(TOut);
+    }
   const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
 
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
   half8 kn[4], qb[4], mf[4][2], ahi[2], alo[2], kt[2][2];
   floatx4 gam[2], gam_nx[2];  // e^{G_C} of the current and of the next chunk
-  uint16_t vraw[4];
+  uint16_t vraw[NT][4];
 
   // buffer bases advance by a fixed stride per chunk
   const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * kBlockBytes;
@@ -534,15 +552,16 @@ __global__ __launch_bounds__(256) void rec_kernel(
   };
   auto load_kt = [&](rsrc_t r) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
-    }
   };
   auto load_v = [&](int64_t c) {
     const rsrc_t r = make_rsrc(v_base + c * tok_step, rows_bytes(c, 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vraw[i] = __builtin_amdgcn_raw_buffer_load_b16(r, v_off[i], 0, 0);
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vraw[nt][i] = __builtin_amdgcn_raw_buffer_load_b16(r, v_off[nt][i], 0, 0);
   };
 
   if (nc > 0) {  // same issue order as in the loop, so the loop's memory waits stay partial
@@ -556,116 +575,130 @@ __global__ __launch_bounds__(256) void rec_kernel(
   int buf = 0;
   for (int64_t c = 0; c < nc; ++c) {
     // operands of the next chunk are loaded right after their use in this one (the last
-    // chunk reloads itself), unconditionally, so every load has a chunk's time to land
+    // chunk reloads itself), unconditionally and in a fixed order, so every load has a
+    // chunk's time to land and the loop carries no branch
     const int64_t cn = min(c + 1, nc - 1);
     const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
     gam[0] = gam_nx[0];
     gam[1] = gam_nx[1];
-    // -- all-gather the state strip in fp16
+    // -- all-gather the state strips in fp16
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-      half4 hv;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[u][i]);
-      *reinterpret_cast<half4*>(&sx[buf][nn][32 * w + 16 * u + 4 * gq]) = hv;
-    }
+      for (int u = 0; u < 2; ++u) {
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
+        *reinterpret_cast<half4*>(&sx[buf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
+      }
     __syncthreads();
     // -- complete -Kbar S and Qbar S for this wave's 16 chunk rows
-    floatx4 X = zero, QS = zero;
+    floatx4 X[NT], QS[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) X[nt] = QS[nt] = zero;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      half8 bs;
-      const _Float16* sp = &sx[buf][nn][32 * j + 4 * gq];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bs[i] = sp[i];
-        bs[i + 4] = sp[16 + i];
+      for (int nt = 0; nt < NT; ++nt) {
+        half8 bs;
+        const _Float16* sp = &sx[buf][16 * nt + nn][32 * j + 4 * gq];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bs[i] = sp[i];
+          bs[i + 4] = sp[16 + i];
+        }
+        X[nt] = mfma_f16(kn[j], bs, X[nt]);
+        QS[nt] = mfma_f16(qb[j], bs, QS[nt]);
       }
-      X = mfma_f16(kn[j], bs, X);
-      QS = mfma_f16(qb[j], bs, QS);
     }
     load_kq(rn);
     // -- Y = V - Kbar S for this wave's rows, all-gathered in fp16
-    {
-      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       half4 hy;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hy[i] = static_cast<_Float16>(X[i] + bf16_bits_to_f32(vraw[i]));
-      *reinterpret_cast<half4*>(&yx[buf][nn][16 * w + 4 * gq]) = hy;
+      for (int i = 0; i < 4; ++i) hy[i] = static_cast<_Float16>(X[nt][i] + bf16_bits_to_f32(vraw[nt][i]));
+      *reinterpret_cast<half4*>(&yx[buf][16 * nt + nn][16 * w + 4 * gq]) = hy;
     }
     load_v(cn);
     __syncthreads();
-    // -- U' = M Y, all 64 rows (each wave keeps a full copy)
-    floatx4 U[4];
-    {
+    // -- U' = M Y, all 64 rows (each wave keeps a full copy), split into fp16 hi + lo
+    half8 uh[NT][2], ul[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       half8 by[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const _Float16* yp = &yx[buf][nn][32 * ks + 4 * gq];
+        const _Float16* yp = &yx[buf][16 * nt + nn][32 * ks + 4 * gq];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           by[ks][i] = yp[i];
           by[ks][i + 4] = yp[16 + i];
         }
       }
+      floatx4 U[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         U[mt] = mfma_f16(mf[mt][0], by[0], zero);
         U[mt] = mfma_f16(mf[mt][1], by[1], U[mt]);
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          _Float16 hh, ll;
+          split_f16(i < 4 ? U[2 * ks][i] : U[2 * ks + 1][i - 4], hh, ll);
+          uh[nt][ks][i] = hh;
+          ul[nt][ks][i] = ll;
+        }
     }
     load_m(rn);
-    half8 uh[2], ul[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        _Float16 hh, ll;
-        split_f16(i < 4 ? U[2 * ks][i] : U[2 * ks + 1][i - 4], hh, ll);
-        uh[ks][i] = hh;
-        ul[ks][i] = ll;
-      }
-    // -- outputs of this wave's rows: Qbar S + Aqk U'
-    // (for rows < 32 the second k-step multiplies the zero upper part of Aqk; it is kept
-    // so that the loop body has no branch and every memory wait stays exact)
-    floatx4 acc = QS;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      acc = mfma_f16(ahi[ks], uh[ks], acc);
-      acc = mfma_f16(ahi[ks], ul[ks], acc);
-      acc = mfma_f16(alo[ks], uh[ks], acc);
-    }
-    load_a(rn);
+    // -- outputs of this wave's rows: Qbar S + Aqk U' (for rows < 32 the second k-step
+    //    multiplies the zero upper part of Aqk; it is kept so the loop body has no branch)
     {
       const rsrc_t ro = make_rsrc(o_base + c * tok_step, rows_bytes(c, (int)sizeof(TOut)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (sizeof(TOut) == 4)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), ro, o_off[i], 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i]), ro, o_off[i], 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        floatx4 acc = QS[nt];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          acc = mfma_f16(ahi[ks], uh[nt][ks], acc);
+          acc = mfma_f16(ahi[ks], ul[nt][ks], acc);
+          acc = mfma_f16(alo[ks], uh[nt][ks], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (sizeof(TOut) == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), ro, o_off[nt][i], 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i]), ro, o_off[nt][i], 0, 0);
+        }
       }
     }
+    load_a(rn);
     // -- this wave's state rows: S = Diag(e^{G_C}) S + Ktil^T U'
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      s[u] *= gam[u];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        s[u] = mfma_f16(kt[u][ks], uh[ks], s[u]);
-        s[u] = mfma_f16(kt[u][ks], ul[ks], s[u]);
+      for (int u = 0; u < 2; ++u) {
+        s[nt][u] *= gam[u];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          s[nt][u] = mfma_f16(kt[u][ks], uh[nt][ks], s[nt][u]);
+          s[nt][u] = mfma_f16(kt[u][ks], ul[nt][ks], s[nt][u]);
+        }
       }
-    }
     load_kt(rn);
     buf ^= 1;
   }
   if (S_T) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col] = s[u][i];
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
   }
 }
 
@@ -705,15 +738,34 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
                        static_cast<const uint16_t*>(p.g), static_cast<const uint16_t*>(p.beta),
                        p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, ws);
   const int64_t pairs = (int64_t)p.n_seq * p.H;
-  const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * NSTRIP;
-  if (p.out_bf16)
-    hipLaunchKernelGGL(rec_kernel<uint16_t>, dim3((unsigned)rec_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.v), p.S0, static_cast<uint16_t*>(p.o),
-                       p.S_T, p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws);
-  else
-    hipLaunchKernelGGL(rec_kernel<float>, dim3((unsigned)rec_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.v), p.S0, static_cast<float*>(p.o), p.S_T,
-                       p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws);
+  // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
+  // workgroup maximises parallelism. Many pairs (at least four strip workgroups per CU): two
+  // strips per workgroup halve the operand traffic per column.
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  const bool two = pairs * NSTRIP >= 4LL * n_cu;
+  const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
+  const dim3 grid((unsigned)rec_blocks), block(256);
+  const uint16_t* vv = static_cast<const uint16_t*>(p.v);
+  const int64_t mc = max_chunks(p);
+  if (p.out_bf16) {
+    uint16_t* oo = static_cast<uint16_t*>(p.o);
+    if (two)
+      hipLaunchKernelGGL((rec_kernel<uint16_t, 2>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+    else
+      hipLaunchKernelGGL((rec_kernel<uint16_t, 1>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+  } else {
+    float* oo = static_cast<float*>(p.o);
+    if (two)
+      hipLaunchKernelGGL((rec_kernel<float, 2>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+    else
+      hipLaunchKernelGGL((rec_kernel<float, 1>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+  }
   return hipGetLastError();
 }
 

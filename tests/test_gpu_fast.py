@@ -34,6 +34,8 @@ CASES = {
     "prefill-4k T=300 H=2": lambda: inputs.make_prefill(1, T=300, H=2),
     "prefill-64k-bound T=1024 H=4": lambda: inputs.make_prefill(2, T=1024, H=4),
     "ragged varlen": ragged_case,
+    # 224 (sequence, head) pairs: enough workgroups that each one takes two column strips
+    "ragged varlen H=32 (two strips per workgroup)": lambda: ragged_case(H=32),
     "dense batch B=3 T=130": dense_batch_case,
     "no initial state": lambda: _no_s0(inputs.make_prefill(1, T=200, H=2)),
 }
