@@ -5,7 +5,8 @@
 A step is one kda_chunk_fwd (prefill: cumulative decay, tile products, the (I + A)
 inverse, state propagation and outputs) over one batch of the workload, inputs already
 resident on the GPU. K steps are timed between two device synchronisations; every launch
-is also bracketed by HIP events on the stream it runs on. The decode half of the metric
+is also bracketed by HIP events on the stream it runs on. A further --cold-steps launches
+are timed one by one after a cache flush each (secondary figure). The decode half of the metric
 (GB/s against HBM peak) is measured in the same run on the decode workload (N=512
 sequences, H=32, 1 GiB fp32 state updated in place), from its own timed loop.
 
@@ -87,6 +88,25 @@ def time_launches(fn, steps, warmup, stream):
     return wall, [a.elapsed_time(b) for a, b in ev]
 
 
+def time_cold(fn, steps, stream, flush_bytes=512 << 20):
+    """Per-launch event times with the caches cold: before each launch, outside its event
+    pair, a 512 MiB buffer is overwritten, which evicts the inputs and the workspace from
+    L2 and the 256 MB MALL. Returns (median ms, min ms)."""
+    import torch
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    ms = []
+    for i in range(steps):
+        junk.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return ms[len(ms) // 2], ms[0]
+
+
 def cpu_baseline(x, budget_s=10.0):
     """The oracle (fp64, as committed) on the host cores: whole passes over the workload
     until budget_s has elapsed (at least one)."""
@@ -145,6 +165,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill-4k", choices=list(WORKLOADS))
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra launches timed after a 512 MiB cache flush each (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -189,6 +211,7 @@ def main():
 
     wall, ms = time_launches(step, args.steps, args.warmup, stream)
     per_ms = sum(ms) / len(ms)
+    cold = time_cold(step, args.cold_steps, stream) if args.cold_steps else None
     token_heads = B * T * H
     flops = flops_per_token_head() * token_heads
     nbytes = bytes_per_token_head() * token_heads + 2 * 4 * d * d * n_seq * H
@@ -215,7 +238,9 @@ def main():
                     "alg_tflops": tflops, "alg_mfma_frac": tflops / MFMA_PEAK_TFLOPS,
                     "alg_GB_per_s": gbs, "alg_hbm_frac": gbs / HBM_PEAK_GBS,
                     "attainable_frac": (flops / (per_ms * 1e-3)) / attainable,
-                    "workspace_bytes": nbytes_ws},
+                    "workspace_bytes": nbytes_ws,
+                    "cold_event_ms_median": cold and cold[0], "cold_event_ms_min": cold and cold[1],
+                    "cold_steps": args.cold_steps},
         "roofline": {"kernel": "kda_chunk_fwd launch (prep_kernel + rec_kernel)", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
