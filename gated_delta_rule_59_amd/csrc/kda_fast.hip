@@ -2,16 +2,21 @@
 //
 // The chunked algebra (from the recurrence S_r = (I - b_r k_r k_r^T) D_r S_{r-1} + b_r k_r v_r^T)
 // for a 64-token chunk entered with state S, G_r = sum_{j<=r} g_j per key channel:
-//   U' = M (V - Kbar S),  M = (I + A)^{-1} diag(b),  A[r][j] = b_r sum_c k_r k_j e^{G_r - G_j} (j < r)
-//   O  = Qbar S + Aqk U', Aqk[r][j] = sum_c q_r k_j e^{G_r - G_j} (j <= r)
-//   S <- Diag(e^{G_C}) S + Ktil^T U',  Kbar = K e^{G}, Qbar = Q e^{G}, Ktil = K e^{G_C - G}.
+//   U' = M (V - Kbar S) = Utilde - W S,   M = (I + A)^{-1} diag(b),  W = M Kbar,  Utilde = M V
+//   A[r][j] = b_r sum_c k_r k_j e^{G_r - G_j} (j < r),   Aqk[r][j] = sum_c q_r k_j e^{G_r - G_j} (j <= r)
+//   O  = Qbar S + Aqk U' = Qhat S + Ohat,   Qhat = Qbar - Aqk W,   Ohat = Aqk Utilde
+//   S <- Diag(e^{G_C}) S + Ktil^T U',      Kbar = K e^{G}, Qbar = Q e^{G}, Ktil = K e^{G_C - G}.
+// Everything that does not depend on the entry state (W, Utilde, Qhat, Ohat, Ktil) is formed
+// for all chunks in parallel; the serial walk over the chunks then needs two products with
+// the state per chunk (W S for U', Qhat S for the outputs) and the state update.
 //
 // Two kernels.
 //  prep_kernel (one workgroup per chunk and head, all chunks in parallel): the per-channel
 //    cumulative log-decay; A and Aqk on the matrix cores; the inverse (I + A)^{-1} by
-//    blocked forward substitution in LDS; and every operand the recurrence needs, stored
-//    in the workspace already in MFMA lane order ("fragments", 1 KiB = 64 lanes x 8 fp16)
-//    so that each later load is one coalesced 16-byte load per lane.
+//    blocked forward substitution in LDS; then W, Utilde, Qhat, Ohat on the matrix cores.
+//    Results are stored in the workspace already in MFMA lane order, so each later load is
+//    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
+//    and result tiles (1 KiB = 64 lanes x 4 fp32).
 //    A and Aqk are built from 16-token tiles whose exponent is measured from the state before
 //    the row tile: the row factor e^{G_r - ref} lies in [e^-80, 1] and the column factor
 //    e^{ref - G_j} is <= 1 off the diagonal and in [1, e^80] on it, because each step's
@@ -21,13 +26,12 @@
 //    bf16 hi + lo pairs (three products) to keep 16 bits of precision. Off-diagonal factors
 //    are <= 1 and use fp16 (11-bit significand) directly.
 //  rec_kernel (one workgroup per sequence, head and 16 value columns, serial over chunks):
-//    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence;
-//    four waves split the 128 key rows. Per chunk: the state strip is all-gathered in
-//    fp16 through LDS, each wave forms complete Kbar S and Qbar S for its own 16 chunk rows,
-//    Y = V - Kbar S is all-gathered, U' = M Y, then the outputs Qbar S + Aqk U' (Aqk and U'
-//    split into fp16 hi + lo) and the wave's rows of the state update. Columns of S evolve independently
-//    (the transition acts on the key side only), so splitting the value columns over
-//    workgroups is exact and needs no communication.
+//    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence.
+//    Eight waves in two roles. Waves 0-3 own 32 key rows of the state each and carry the
+//    dependency chain: U' = Utilde - W S for their 16 chunk rows, then the state update.
+//    Waves 4-7 compute the outputs Qhat S + Ohat of their 16 chunk rows from the same
+//    gathered state, off the chain. Columns of S evolve independently (the transition acts on
+//    the key side only), so splitting the value columns over workgroups is exact.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -41,15 +45,14 @@ constexpr int DV = 128;
 constexpr int NSTRIP = DV / 16;  // 16-column strips per (sequence, head)
 
 // Workspace block of one (chunk, head), byte offsets. Fragment f of a group starts at
-// group + f * 1024; lane l's eight fp16 values at + l * 16.
-constexpr int OFF_KB = 0;        // -Kbar as A operand: [k-step over dk (4)][row tile (4)]
-constexpr int OFF_QB = 16384;    // Qbar, same order
+// group + f * 1024 (lane l's eight fp16 at + l * 16); result tile f likewise (four fp32).
+constexpr int OFF_WN = 0;        // -W as A operand: [k-step over dk (4)][row tile (4)]
+constexpr int OFF_QH = 16384;    // Qhat, same order
 constexpr int OFF_KT = 32768;    // Ktil^T: [dk tile (8)][k-step over chunk rows (2)]
-constexpr int OFF_M = 49152;     // M: [row tile (4)][k-step (2)]
-constexpr int OFF_AHI = 57344;   // Aqk hi: [row tile (4)][k-step (2)]
-constexpr int OFF_ALO = 65536;   // Aqk lo
-constexpr int OFF_GAM = 73728;   // e^{G_C}, fp32 [128]
-constexpr size_t kBlockBytes = 74240;
+constexpr int OFF_UT = 49152;    // Utilde result tiles: [value tile (8)][row tile (4)]
+constexpr int OFF_OH = 81920;    // Ohat, same order
+constexpr int OFF_GAM = 114688;  // e^{G_C}, fp32 [128]
+constexpr size_t kBlockBytes = 115200;
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -112,35 +115,79 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+// x from lane m - S of the same 16-lane DPP row (0 for m < S).
+template <int S>
+__device__ __forceinline__ float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + S, 0xF, 0xF, true));
+}
+// Inclusive prefix sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+__device__ __forceinline__ half8 frag_from_halves(const half4& a, const half4& b) {
+  half8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = a[i];
+    f[i + 4] = b[i];
+  }
+  return f;
+}
+// Fragment (rows r, K slots of a 32-wide k-step) from a [row][k] fp16 array: slot i < 4 is
+// k = 4 gq + i, slot i >= 4 is k = 16 + 4 gq + i - 4.
+__device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
+  return frag_from_halves(*reinterpret_cast<const half4*>(rowp + 4 * gq),
+                          *reinterpret_cast<const half4*>(rowp + 16 + 4 * gq));
+}
+
 // One workgroup per (chunk, head); wave a owns row tile a (chunk rows 16a .. 16a+15). In the
 // MFMA fragment layout lane l of wave a holds row 16a + (l & 15) and, for each of the four
-// 32-channel k-steps, the eight channels 32 ks + kslot(l >> 4, i). Every per-element quantity
-// is formed once, in registers, in that layout:
+// 32-channel k-steps, the eight channels 32 ks + kslot(l >> 4, i). The 16 lanes that share
+// l >> 4 form one DPP row and hold the same channels of the tile's 16 rows, so the per-tile
+// cumulative decay is a 16-lane scan. Every per-element quantity is formed once, in
+// registers, in that layout:
 //   rf = e^{G_r - ref_a}   (ref_a = G at the last token before tile a)   in [e^-80, 1]
 //   cf = e^{Gend_a - G_r}  (Gend_a = G at the last token of tile a)       in [e^-80, 1]
 // The row operand of tile a is k rf (q rf), its diagonal column operand k / rf (in [1, e^80]
 // times k, bf16 range), and the column operand it lends to later tiles b > a is k cf, scaled
 // there by the per-channel factor e^{ref_b - Gend_a} <= 1. Kbar, Qbar and Ktil follow from the
-// same values times per-channel constants.
+// same values times per-channel constants. Products are arranged so that their results land
+// in the lane layout the next product or the workspace needs: a result tile computed as
+// (column operand) x (row operand) leaves each lane with four entries of its own row, which
+// for two adjacent tiles is exactly an A-operand fragment of that row.
 __global__ __launch_bounds__(256, 2) void prep_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
     int n_seq, uint8_t* __restrict__ ws) {
-  constexpr int GSR = DK + 4;   // log2 cumulative decay rows (fp32)
-  constexpr int KTR = C + 8;    // Ktil^T rows (fp16, channel-major)
-  // R1: G (fp32 [64][GSR]) -> Ktil^T (fp16 [128][KTR]) -> A, Aqk (fp32 [64][64] each)
-  // R2: column operands k cf (fp32, fragment order [tile][ks][lane][8]) -> T (fp32 [64][64]), X
-  __shared__ __align__(16) float R1[64 * GSR];
-  __shared__ __align__(16) float R2[4 * 4 * 64 * 8];
-  __shared__ __align__(16) float REF2[4][DK], END2[4][DK], PCH[4][DK], ECH[4][DK], XCH[3][DK];
-  __shared__ float Bs[C];
-  float* Gs = R1;
-  _Float16* KtT = reinterpret_cast<_Float16*>(R1);
-  float* A32 = R1;
-  float* AQ32 = R1 + 64 * 64;
-  float* T32 = R2;
-  float* Xs = R2 + 64 * 64;
+  constexpr int TR = C + 8;         // row stride (fp16) of the channel-major staging arrays
+  constexpr int AS = C + 4;         // row stride (fp32) of A and T
+  constexpr int STG = DK * TR * 2;  // bytes of one staging array
+  // One LDS arena reused phase by phase (byte ranges):
+  //   operands: lent column operands k cf, fp32 [3][4][64][8]          [0, 24576)
+  //             Ktil^T staging, fp16 [channel][row]                     [24576, 43008)
+  //             Kbar^T staging (kept until W is formed)                 [43008, 61440)
+  //   inverse:  A fp32 [64][AS] [0, 17408), T [17408, 34816), scratch [34816, 37888)
+  //   products: V^T staging [0, 18432), once M is in registers
+  //   last:     W^T [0, 18432), Utilde^T hi [18432, 36864), lo [36864, 55296)
+  __shared__ __align__(16) unsigned char arena[61440];
+  __shared__ __align__(16) float TOT[4][DK], PCH[4][DK], ECH[4][DK], XCH[3][DK];
+  __shared__ __align__(16) float Bs[C];
+  float* KC = reinterpret_cast<float*>(arena);
+  _Float16* KTs = reinterpret_cast<_Float16*>(arena + 24576);
+  _Float16* KBs = reinterpret_cast<_Float16*>(arena + 43008);
+  float* A32 = reinterpret_cast<float*>(arena);
+  float* T32 = reinterpret_cast<float*>(arena + 17408);
+  float* Xs = reinterpret_cast<float*>(arena + 34816);
+  _Float16* VTs = reinterpret_cast<_Float16*>(arena);
+  _Float16* WTs = reinterpret_cast<_Float16*>(arena);
+  _Float16* UTh = reinterpret_cast<_Float16*>(arena + STG);
+  _Float16* UTl = reinterpret_cast<_Float16*>(arena + 2 * STG);
 
   const int h = blockIdx.x % H;
   const int64_t cid = blockIdx.x / H;
@@ -169,152 +216,115 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l = t & 63, gq = l >> 4, m = l & 15;
-
-  // this lane's k and q elements (row 16w + m, fragment channels), issued first so their
-  // latency overlaps phase 1
   const int row = 16 * w + m;
   const bool row_ok = row < Cn;
-  u16x4 kraw[4][2], qraw[4][2];
+
+  // ---- this lane's 32 elements of row 16w + m of k, q, g, v (rows past the end read as 0)
+  u16x4 kraw[4][2], qraw[4][2], graw[4][2], vraw[4][2];
+  uint16_t braw;
   {
-    const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
+    const int64_t tr = (tok0 + min(row, Cn - 1)) * H + h;
+    const int64_t erow = tr * DK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t e = erow + 32 * ks + 16 * hf + 4 * gq;
+        graw[ks][hf] = *reinterpret_cast<const u16x4*>(g + e);
+        kraw[ks][hf] = *reinterpret_cast<const u16x4*>(k + e);
+        qraw[ks][hf] = *reinterpret_cast<const u16x4*>(q + e);
+        vraw[ks][hf] = *reinterpret_cast<const u16x4*>(v + e);
+      }
+    braw = beta[tr];
+  }
+  // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
+  float gs[4][8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      gs[ks][i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
+  if (m == 15) {  // the tile's totals
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int c0 = 32 * ks + 4 * gq;
-      kraw[ks][0] = *reinterpret_cast<const u16x4*>(k + erow + c0);
-      kraw[ks][1] = *reinterpret_cast<const u16x4*>(k + erow + c0 + 16);
-      qraw[ks][0] = *reinterpret_cast<const u16x4*>(q + erow + c0);
-      qraw[ks][1] = *reinterpret_cast<const u16x4*>(q + erow + c0 + 16);
+      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 4 * gq]) =
+          floatx4{gs[ks][0], gs[ks][1], gs[ks][2], gs[ks][3]};
+      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 16 + 4 * gq]) =
+          floatx4{gs[ks][4], gs[ks][5], gs[ks][6], gs[ks][7]};
     }
   }
-  // ---- phase 1: g rows into LDS (rows past the end read as 0), beta
+  if (gq == 0) Bs[row] = row_ok ? bf16_bits_to_f32(braw) : 0.f;
+  __syncthreads();
+  // ---- per-channel constants from the tile totals (half the threads per pair of tiles)
   {
-    const int r = t >> 2, cb = t & 3;
-    const bool ok = r < Cn;
-    const int64_t e = ((tok0 + min(r, Cn - 1)) * H + h) * DK + cb * 32;
-    u16x8 gv[4];
-#pragma unroll
-    for (int vv = 0; vv < 4; ++vv) gv[vv] = *reinterpret_cast<const u16x8*>(g + e + 8 * vv);
-    const uint16_t braw = beta[(tok0 + min(t & (C - 1), Cn - 1)) * H + h];
-#pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-      floatx4 lo4, hi4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo4[i] = ok ? bf16_bits_to_f32(gv[vv][i]) : 0.f;
-        hi4[i] = ok ? bf16_bits_to_f32(gv[vv][i + 4]) : 0.f;
-      }
-      *reinterpret_cast<floatx4*>(&Gs[r * GSR + cb * 32 + 8 * vv]) = lo4;
-      *reinterpret_cast<floatx4*>(&Gs[r * GSR + cb * 32 + 8 * vv + 4]) = hi4;
-    }
-    if (t < C) Bs[t] = (t < Cn) ? bf16_bits_to_f32(braw) : 0.f;
-  }
-  __syncthreads();
-  // ---- cumulative log-decay per channel (log2 units) and the per-channel constants
-  if (t < DK) {
-    float col[C];
-#pragma unroll
-    for (int r = 0; r < C; ++r) col[r] = Gs[r * GSR + t];
-    float acc = 0.f;
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-      acc += col[r];
-      col[r] = acc * kLog2e;
-      Gs[r * GSR + t] = col[r];
-    }
-    float ref[4], end[4];
+    const int c = t & (DK - 1), hf = t >> 7;
+    const float t0 = TOT[0][c], t1 = TOT[1][c], t2 = TOT[2][c], t3 = TOT[3][c];
+    const float ref[4] = {0.f, t0, t0 + t1, t0 + t1 + t2};
+    const float tt[4] = {t0, t1, t2, t3};
+    const float gc = ref[3] + t3;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      ref[a] = a ? col[16 * a - 1] : 0.f;
-      end[a] = col[16 * a + 15];
+      if ((a >> 1) != hf) continue;
+      PCH[a][c] = exp2f(ref[a]);               // e^{ref_a}: Kbar = (k rf) e^{ref_a}
+      ECH[a][c] = exp2f(gc - (ref[a] + tt[a]));  // e^{G_C - Gend_a}: Ktil = (k cf) e^{G_C - Gend_a}
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      REF2[a][t] = ref[a];
-      END2[a][t] = end[a];
-      PCH[a][t] = exp2f(ref[a]);             // e^{ref_a}: Kbar = (k rf) e^{ref_a}
-      ECH[a][t] = exp2f(end[3] - end[a]);    // e^{G_C - Gend_a}: Ktil = (k cf) e^{G_C - Gend_a}
+    if (hf == 0) {
+      XCH[0][c] = exp2f(t1);       // column factor of block (2, 0): e^{ref_2 - Gend_0}
+      XCH[1][c] = exp2f(t1 + t2);  // (3, 0)
+      reinterpret_cast<float*>(blk + OFF_GAM)[c] = exp2f(gc);
+    } else {
+      XCH[2][c] = exp2f(t2);       // (3, 1)
     }
-    XCH[0][t] = exp2f(end[1] - end[0]);      // column factor of block (2, 0)
-    XCH[1][t] = exp2f(end[2] - end[0]);      // (3, 0)
-    XCH[2][t] = exp2f(end[2] - end[1]);      // (3, 1)
-    reinterpret_cast<float*>(blk + OFF_GAM)[t] = exp2f(end[3]);
   }
   __syncthreads();
-  // ---- phase 2: this lane's 32 elements of row 16w + m (k, q loaded before phase 1)
+  // ---- per-element factors and operands
   float kr[4][8], qr[4][8], kd[4][8];  // k rf, q rf, k / rf
+  half8 qbar[4];                       // Qbar as A-operand fragments of row tile w
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int c0 = 32 * ks + 4 * gq;
-    const u16x4 k0 = kraw[ks][0], k1 = kraw[ks][1], q0 = qraw[ks][0], q1 = qraw[ks][1];
-    const floatx4 g0 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0]);
-    const floatx4 g1 = *reinterpret_cast<const floatx4*>(&Gs[row * GSR + c0 + 16]);
-    const floatx4 r0 = *reinterpret_cast<const floatx4*>(&REF2[w][c0]);
-    const floatx4 r1 = *reinterpret_cast<const floatx4*>(&REF2[w][c0 + 16]);
-    const floatx4 e0 = *reinterpret_cast<const floatx4*>(&END2[w][c0]);
-    const floatx4 e1 = *reinterpret_cast<const floatx4*>(&END2[w][c0 + 16]);
-    const floatx4 p0 = *reinterpret_cast<const floatx4*>(&PCH[w][c0]);
-    const floatx4 p1 = *reinterpret_cast<const floatx4*>(&PCH[w][c0 + 16]);
-    half8 knf, qbf;
-    floatx4 kc0, kc1;
+    floatx4 tw[2], pe[2], ee[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int c0 = 32 * ks + 16 * hf + 4 * gq;
+      tw[hf] = *reinterpret_cast<const floatx4*>(&TOT[w][c0]);
+      pe[hf] = *reinterpret_cast<const floatx4*>(&PCH[w][c0]);
+      ee[hf] = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
+    }
+    floatx4 kc[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = i & 3;
-      const float kv = row_ok ? bf16_bits_to_f32(i < 4 ? k0[j] : k1[j]) : 0.f;
-      const float qv = row_ok ? bf16_bits_to_f32(i < 4 ? q0[j] : q1[j]) : 0.f;
-      const float gg = i < 4 ? g0[j] : g1[j];
-      const float rf = exp2f(gg - (i < 4 ? r0[j] : r1[j]));
-      const float cf = exp2f((i < 4 ? e0[j] : e1[j]) - gg);
+      const int hf = i >> 2, j = i & 3;
+      const int ch = 32 * ks + 16 * hf + 4 * gq + j;
+      const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
+      const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
+      const float s = gs[ks][i];
+      const float rf = exp2f(s);
+      const float cf = exp2f(tw[hf][j] - s);
       kr[ks][i] = kv * rf;
       qr[ks][i] = qv * rf;
       kd[ks][i] = kv * __builtin_amdgcn_rcpf(rf);
-      const float kcv = kv * cf;
-      if (i < 4) kc0[j] = kcv; else kc1[j] = kcv;
-      const float pe = i < 4 ? p0[j] : p1[j];
-      knf[i] = static_cast<_Float16>(-kr[ks][i] * pe);
-      qbf[i] = static_cast<_Float16>(qr[ks][i] * pe);
+      kc[hf][j] = kv * cf;
+      qbar[ks][i] = static_cast<_Float16>(qr[ks][i] * pe[hf][j]);
+      KBs[ch * TR + row] = static_cast<_Float16>(kr[ks][i] * pe[hf][j]);
+      KTs[ch * TR + row] = static_cast<_Float16>(kc[hf][j] * ee[hf][j]);
     }
-    // Kbar (negated) and Qbar fragments [ks][row tile w]
-    *reinterpret_cast<half8*>(blk + OFF_KB + (ks * 4 + w) * 1024 + l * 16) = knf;
-    *reinterpret_cast<half8*>(blk + OFF_QB + (ks * 4 + w) * 1024 + l * 16) = qbf;
-    // column operand k cf lent to later row tiles
-    float* kcp = R2 + ((w * 4 + ks) * 64 + l) * 8;
-    *reinterpret_cast<floatx4*>(kcp) = kc0;
-    *reinterpret_cast<floatx4*>(kcp + 4) = kc1;
-  }
-  __syncthreads();  // every wave has read G: R1 is reused for Ktil^T
-  // Ktil = (k cf) e^{G_C - Gend_w}, transposed to channel-major for its fragments
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const float* kcp = R2 + ((w * 4 + ks) * 64 + l) * 8;
-    const int c0 = 32 * ks + 4 * gq;
-    const floatx4 v0 = *reinterpret_cast<const floatx4*>(kcp);
-    const floatx4 v1 = *reinterpret_cast<const floatx4*>(kcp + 4);
-    const floatx4 x0 = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
-    const floatx4 x1 = *reinterpret_cast<const floatx4*>(&ECH[w][c0 + 16]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      KtT[(c0 + i) * KTR + row] = static_cast<_Float16>(v0[i] * x0[i]);
-      KtT[(c0 + 16 + i) * KTR + row] = static_cast<_Float16>(v1[i] * x1[i]);
+    if (w < 3) {  // column operand k cf lent to later row tiles
+      float* kcp = KC + ((w * 4 + ks) * 64 + l) * 8;
+      *reinterpret_cast<floatx4*>(kcp) = kc[0];
+      *reinterpret_cast<floatx4*>(kcp + 4) = kc[1];
     }
   }
   __syncthreads();
-  // ---- Ktil^T fragments [dk tile][ks over chunk rows]: four per wave
+  // ---- Ktil^T fragments [dk tile][k-step over chunk rows]: four per wave
 #pragma unroll
   for (int jf = 0; jf < 4; ++jf) {
     const int f = w * 4 + jf;
     const int mt = f >> 1, ks = f & 1;
-    const _Float16* src = KtT + (16 * mt + m) * KTR + 32 * ks + 4 * gq;
-    const half4 a0 = *reinterpret_cast<const half4*>(src);
-    const half4 a1 = *reinterpret_cast<const half4*>(src + 16);
-    half8 kt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kt[i] = a0[i];
-      kt[i + 4] = a1[i];
-    }
-    *reinterpret_cast<half8*>(blk + OFF_KT + f * 1024 + l * 16) = kt;
+    *reinterpret_cast<half8*>(blk + OFF_KT + f * 1024 + l * 16) =
+        lds_frag(KTs + (16 * mt + m) * TR + 32 * ks, gq);
   }
-  // ---- A = beta K K^T and Aqk = Q K^T tiles of row tile w on the matrix cores
+  // ---- A and Aqk tiles of row tile w. Each tile is computed as (column operand) x (row
+  //      operand), i.e. transposed, so lane l ends with entries (16w + l&15, 16bb + 4 gq + i).
   floatx4 akk[4], aqk[4];
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) akk[bb] = aqk[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -332,17 +342,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       split_bf16(kd[ks][i], hh, ll); ch[i] = hh; cl[i] = ll;
     }
     // diagonal tile: column factor up to e^80, split bf16
-    akk[w] = mfma_bf16(rkh, ch, akk[w]);
-    akk[w] = mfma_bf16(rkh, cl, akk[w]);
-    akk[w] = mfma_bf16(rkl, ch, akk[w]);
-    aqk[w] = mfma_bf16(rqh, ch, aqk[w]);
-    aqk[w] = mfma_bf16(rqh, cl, aqk[w]);
-    aqk[w] = mfma_bf16(rql, ch, aqk[w]);
+    akk[w] = mfma_bf16(ch, rkh, akk[w]);
+    akk[w] = mfma_bf16(ch, rkl, akk[w]);
+    akk[w] = mfma_bf16(cl, rkh, akk[w]);
+    aqk[w] = mfma_bf16(ch, rqh, aqk[w]);
+    aqk[w] = mfma_bf16(ch, rql, aqk[w]);
+    aqk[w] = mfma_bf16(cl, rqh, aqk[w]);
     // earlier tiles: factors <= 1, fp16
 #pragma unroll
     for (int bb = 0; bb < 3; ++bb) {
       if (bb >= w) break;
-      const float* kcp = R2 + ((bb * 4 + ks) * 64 + l) * 8;
+      const float* kcp = KC + ((bb * 4 + ks) * 64 + l) * 8;
       const floatx4 c0 = *reinterpret_cast<const floatx4*>(kcp);
       const floatx4 c1 = *reinterpret_cast<const floatx4*>(kcp + 4);
       floatx4 x0 = {1.f, 1.f, 1.f, 1.f}, x1 = x0;
@@ -357,36 +367,49 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         c16[i] = static_cast<_Float16>(c0[i] * x0[i]);
         c16[i + 4] = static_cast<_Float16>(c1[i] * x1[i]);
       }
-      akk[bb] = mfma_f16(rk16, c16, akk[bb]);
-      aqk[bb] = mfma_f16(rq16, c16, aqk[bb]);
+      akk[bb] = mfma_f16(c16, rk16, akk[bb]);
+      aqk[bb] = mfma_f16(c16, rq16, aqk[bb]);
     }
   }
-  __syncthreads();  // Ktil^T and the lent column operands are dead: R1, R2 reused
+  __syncthreads();  // the lent operands and Ktil^T staging are dead: A and T take the arena
+  // ---- beta-scaled A rows into LDS (entries on or above the diagonal are never read);
+  //      Aqk (lower, diagonal included) as A-operand fragments hi + lo in registers
+  {
+    const float br = Bs[row];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * gq + i, jc = 16 * bb + m;
-      A32[r * 64 + jc] = (bb <= w && jc < r) ? Bs[r] * akk[bb][i] : 0.f;
-      AQ32[r * 64 + jc] = (bb <= w && jc <= r) ? aqk[bb][i] : 0.f;
-    }
+    for (int bb = 0; bb < 4; ++bb)
+      if (bb <= w) *reinterpret_cast<floatx4*>(&A32[row * AS + 16 * bb + 4 * gq]) = br * akk[bb];
   }
-  for (int i = t; i < 64 * 64; i += 256) T32[i] = 0.f;
+  half8 ahi[2], alo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int bb = 2 * ks + (i >> 2), ii = i & 3;
+      const float a = (bb < w || (bb == w && 4 * gq + ii <= m)) ? aqk[bb][ii] : 0.f;
+      _Float16 hh, ll;
+      split_f16(a, hh, ll);
+      ahi[ks][i] = hh;
+      alo[ks][i] = ll;
+    }
   __syncthreads();
   // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by substitution (wave w, lane = column)
   if (l < 16) {
     const int j = l, o = 16 * w;
+    // entries of column j above the diagonal are zero, so every term of the substitution
+    // can be summed unconditionally (row values are the same for all lanes)
     float col[16];
+    col[0] = j == 0 ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 1; i < 16; ++i) {
+      const float* arow = A32 + (o + i) * AS + o;
       float sacc = 0.f;
 #pragma unroll
-      for (int mm = 0; mm < i; ++mm)
-        if (mm >= j) sacc += A32[(o + i) * 64 + o + mm] * col[mm];
-      col[i] = (i < j) ? 0.f : (i == j ? 1.f : -sacc);
+      for (int mm = 0; mm < i; ++mm) sacc = fmaf(arow[mm], col[mm], sacc);
+      col[i] = i == j ? 1.f : -sacc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) T32[(o + i) * 64 + o + j] = col[i];
+    for (int i = 0; i < 16; ++i) T32[(o + i) * AS + o + j] = col[i];
   }
   __syncthreads();
   // ---- off-diagonal blocks, by distance from the diagonal:
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         for (int cc = bb; cc < a; ++cc)
 #pragma unroll
           for (int mm = 0; mm < 16; ++mm)
-            x += A32[(16 * a + i) * 64 + 16 * cc + mm] * T32[(16 * cc + mm) * 64 + 16 * bb + jj];
+            x += A32[(16 * a + i) * AS + 16 * cc + mm] * T32[(16 * cc + mm) * AS + 16 * bb + jj];
         Xs[(a - L) * 256 + i * 16 + jj] = x;
       }
       __syncthreads();
@@ -410,36 +433,107 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         float x = 0.f;
 #pragma unroll
         for (int mm = 0; mm < 16; ++mm)
-          x += T32[(16 * a + i) * 64 + 16 * a + mm] * Xs[(a - L) * 256 + mm * 16 + jj];
-        T32[(16 * a + i) * 64 + 16 * bb + jj] = -x;
+          x += T32[(16 * a + i) * AS + 16 * a + mm] * Xs[(a - L) * 256 + mm * 16 + jj];
+        T32[(16 * a + i) * AS + 16 * bb + jj] = -x;
       }
       __syncthreads();
     }
   }
-  // ---- M = T diag(beta) and Aqk hi/lo fragments: [row tile][ks]
+  // ---- M = T diag(beta): A-operand fragments of row tile w (blocks right of it are zero)
+  half8 mfr[2];
 #pragma unroll
-  for (int jf = 0; jf < 2; ++jf) {
-    const int f = (t >> 6) + 4 * jf;  // 0..7
-    const int mt = f >> 1, ks = f & 1;
-    const int rr = 16 * mt + m;
-    half8 mf, ah, al;
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int bb = 2 * ks + hf;
+      const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[row * AS + 16 * bb + 4 * gq]);
+      const floatx4 bv = *reinterpret_cast<const floatx4*>(&Bs[16 * bb + 4 * gq]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        mfr[ks][4 * hf + ii] = static_cast<_Float16>(bb <= w ? tv[ii] * bv[ii] : 0.f);
+    }
+  __syncthreads();  // T is in registers: V^T takes the front of the arena
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int cc = 32 * ks + kslot(gq, i);
-      mf[i] = static_cast<_Float16>(T32[rr * 64 + cc] * Bs[cc]);
-      _Float16 hh, ll;
-      split_f16(AQ32[rr * 64 + cc], hh, ll);
-      ah[i] = hh;
-      al[i] = ll;
+      const int ch = 32 * ks + 16 * (i >> 2) + 4 * gq + (i & 3);
+      VTs[ch * TR + row] =
+          static_cast<_Float16>(row_ok ? bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]) : 0.f);
     }
-    *reinterpret_cast<half8*>(blk + OFF_M + f * 1024 + l * 16) = mf;
-    *reinterpret_cast<half8*>(blk + OFF_AHI + f * 1024 + l * 16) = ah;
-    *reinterpret_cast<half8*>(blk + OFF_ALO + f * 1024 + l * 16) = al;
+  __syncthreads();
+  // ---- W = M Kbar (as W^T = Kbar^T M^T, which leaves each lane with its own row) and
+  //      Utilde = M V, row tile w, every 16-column tile
+  half4 wq[8];              // W rounded to fp16: row 16w + m, channels 16ct + 4gq + i
+  half4 uth[8], utl[8];     // Utilde hi + lo: rows 16w + 4gq + i, column 16ct + m
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    floatx4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      aw = mfma_f16(lds_frag(KBs + (16 * ct + m) * TR + 32 * ks, gq), mfr[ks], aw);
+      au = mfma_f16(mfr[ks], lds_frag(VTs + (16 * ct + m) * TR + 32 * ks, gq), au);
+    }
+    *reinterpret_cast<floatx4*>(blk + OFF_UT + (ct * 4 + w) * 1024 + l * 16) = au;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wq[ct][i] = static_cast<_Float16>(aw[i]);
+      _Float16 hh, ll;
+      split_f16(au[i], hh, ll);
+      uth[ct][i] = hh;
+      utl[ct][i] = ll;
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    *reinterpret_cast<half8*>(blk + OFF_WN + (kk * 4 + w) * 1024 + l * 16) =
+        -frag_from_halves(wq[2 * kk], wq[2 * kk + 1]);
+  __syncthreads();  // Kbar^T and V^T are dead: W^T and Utilde^T take the arena
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) WTs[(16 * ct + 4 * gq + i) * TR + row] = wq[ct][i];
+    *reinterpret_cast<half4*>(&UTh[(16 * ct + m) * TR + 16 * w + 4 * gq]) = uth[ct];
+    *reinterpret_cast<half4*>(&UTl[(16 * ct + m) * TR + 16 * w + 4 * gq]) = utl[ct];
+  }
+  __syncthreads();
+  // ---- Qhat = Qbar - Aqk W (via (Aqk W)^T = W^T Aqk^T, own rows again) and Ohat = Aqk Utilde
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    floatx4 aw[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ct = 2 * kk + hf;
+      aw[hf] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 wf = lds_frag(WTs + (16 * ct + m) * TR + 32 * ks, gq);
+        aw[hf] = mfma_f16(wf, ahi[ks], aw[hf]);
+        aw[hf] = mfma_f16(wf, alo[ks], aw[hf]);
+      }
+    }
+    half8 qh;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - aw[i >> 2][i & 3]);
+    *reinterpret_cast<half8*>(blk + OFF_QH + (kk * 4 + w) * 1024 + l * 16) = qh;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    floatx4 ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const half8 uh = lds_frag(UTh + (16 * ct + m) * TR + 32 * ks, gq);
+      const half8 ul = lds_frag(UTl + (16 * ct + m) * TR + 32 * ks, gq);
+      ao = mfma_f16(ahi[ks], uh, ao);
+      ao = mfma_f16(ahi[ks], ul, ao);
+      ao = mfma_f16(alo[ks], uh, ao);
+    }
+    *reinterpret_cast<floatx4*>(blk + OFF_OH + (ct * 4 + w) * 1024 + l * 16) = ao;
   }
 }
 
 // ---------------------------------------------------------------- rec
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return zero and stores
@@ -451,22 +545,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
+__device__ __forceinline__ floatx4 ld_tile(rsrc_t r, int lane_off, int off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
+}
 
 template <typename TOut, int NT>
-__global__ __launch_bounds__(256) void rec_kernel(
-    const uint16_t* __restrict__ v, const float* __restrict__ S0, TOut* __restrict__ o,
-    float* __restrict__ S_T, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    int T, int H, int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
-  // A workgroup owns NT strips of 16 value columns; every operand fragment a wave loads
-  // feeds NT matrix products. Two fp16 exchanges per chunk, double-buffered: the state
-  // strips (all 128 key rows), so every wave can form complete Kbar S and Qbar S for its own
-  // 16 chunk rows, and Y = V - Kbar S (all 64 chunk rows) for U' = M Y. Both are stored
-  // column-major ([column][row]) so the rows a lane needs for a B operand are contiguous,
-  // with rows padded by 8 halves against bank conflicts.
+__global__ __launch_bounds__(512) void rec_kernel(
+    const float* __restrict__ S0, TOut* __restrict__ o, float* __restrict__ S_T,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
+    int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
+  // A workgroup owns NT strips of 16 value columns. Two fp16 exchanges per chunk through
+  // LDS, each followed by a barrier: the state strips (all 128 key rows), which every wave
+  // needs whole for W S or Qhat S of its 16 chunk rows, and U' (all 64 chunk rows) for the
+  // state update. Both are stored column-major ([column][row]) so the rows a lane needs for
+  // a B operand are contiguous, with rows padded by 8 halves against bank conflicts. One
+  // buffer of each suffices: every read of a buffer happens between the barrier after its
+  // write and the next barrier, which precedes its next write.
   constexpr int NG = NSTRIP / NT;  // strip groups per (sequence, head)
-  constexpr int SR = DK + 8, YR = C + 8;
-  __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];
-  __shared__ __align__(16) _Float16 yx[2][NT * 16][YR];
+  constexpr int SR = DK + 8, UR = C + 8;
+  __shared__ __align__(16) _Float16 sx[NT * 16][SR];
+  __shared__ __align__(16) _Float16 ux[2][NT * 16][UR];
 
   // XCD-aware placement: the strip groups of one (sequence, head) share an XCD and its L2.
   const int b = blockIdx.x;
@@ -480,225 +578,182 @@ __global__ __launch_bounds__(256) void rec_kernel(
   const int64_t nc = max((int64_t)0, min((si.len + C - 1) / C, max_chunks - si.cid0));
 
   const int t = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int w = wave & 3;
   const int l = t & 63, gq = l >> 4, nn = l & 15;
-  const int64_t s_base = pair * DK * DV;
-  const int row_stride = H * DV;  // elements between consecutive tokens
-  int col[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) col[nt] = 16 * (NT * sg + nt) + nn;
-
-  // this wave's state rows 32w + 16u + 4gq + i (u = 0, 1), columns col[nt]
-  floatx4 s[NT][2];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[nt][u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] : 0.f;
-
-  // per-lane byte offsets, fixed for the whole sequence
   const int frag_off = l * 16;
-  int v_off[NT][4], o_off[NT][4];  // this wave's chunk rows 16w + 4gq + i
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + col[nt]) * 2;
-      o_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + col[nt]) * (int)sizeof(TOut);
-    }
-  const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
-
-  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-  half8 kn[4], qb[4], mf[4][2], ahi[2], alo[2], kt[2][2];
-  floatx4 gam[2], gam_nx[2];  // e^{G_C} of the current and of the next chunk
-  uint16_t vraw[NT][4];
-
-  // buffer bases advance by a fixed stride per chunk
   const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * kBlockBytes;
   const size_t blk_step = (size_t)H * kBlockBytes;
-  const uint16_t* v_base = v + (si.tok0 * H + h) * DV;
-  TOut* o_base = o + (si.tok0 * H + h) * DV;
-  const size_t tok_step = (size_t)C * row_stride;
-  // bytes of the chunk's rows of this head, up to the end of its last valid row
-  auto rows_bytes = [&](int64_t c, int elem) -> int64_t {
-    const int64_t rows = min((int64_t)C, si.len - c * C);
-    return ((rows - 1) * row_stride + DV) * elem;
-  };
 
-  auto load_kq = [&](rsrc_t r) {  // this wave's row tile, all four dk k-steps; e^{G_C}
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kn[j] = ld_frag(r, frag_off, OFF_KB + (j * 4 + w) * 1024);
-      qb[j] = ld_frag(r, frag_off, OFF_QB + (j * 4 + w) * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      gam_nx[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, gam_off, 64 * u, 0));
-  };
-  auto load_m = [&](rsrc_t r) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) mf[mt][ks] = ld_frag(r, frag_off, OFF_M + (mt * 2 + ks) * 1024);
-  };
-  auto load_a = [&](rsrc_t r) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ahi[ks] = ld_frag(r, frag_off, OFF_AHI + (w * 2 + ks) * 1024);
-      alo[ks] = ld_frag(r, frag_off, OFF_ALO + (w * 2 + ks) * 1024);
-    }
-  };
-  auto load_kt = [&](rsrc_t r) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
-  };
-  auto load_v = [&](int64_t c) {
-    const rsrc_t r = make_rsrc(v_base + c * tok_step, rows_bytes(c, 2));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vraw[nt][i] = __builtin_amdgcn_raw_buffer_load_b16(r, v_off[nt][i], 0, 0);
-  };
+  // B operand of state strip nt for key rows 32 j + kslot(gq, i), column nn
+  auto state_frag = [&](int nt, int j) { return lds_frag(&sx[16 * nt + nn][32 * j], gq); };
 
-  if (nc > 0) {  // same issue order as in the loop, so the loop's memory waits stay partial
-    const rsrc_t r0 = make_rsrc(blk_base, (int64_t)kBlockBytes);
-    load_kq(r0);
-    load_v(0);
-    load_m(r0);
-    load_a(r0);
-    load_kt(r0);
-  }
-  int buf = 0;
-  for (int64_t c = 0; c < nc; ++c) {
-    // operands of the next chunk are loaded right after their use in this one (the last
-    // chunk reloads itself), unconditionally and in a fixed order, so every load has a
-    // chunk's time to land and the loop carries no branch
-    const int64_t cn = min(c + 1, nc - 1);
-    const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
-    gam[0] = gam_nx[0];
-    gam[1] = gam_nx[1];
-    // -- all-gather the state strips in fp16
+  if (wave < 4) {
+    // ------------------------------------------------ state waves: key rows 32w .. 32w+31
+    const int64_t s_base = pair * DK * DV;
+    int col[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        half4 hv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
-        *reinterpret_cast<half4*>(&sx[buf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
-      }
-    __syncthreads();
-    // -- complete -Kbar S and Qbar S for this wave's 16 chunk rows
-    floatx4 X[NT], QS[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) X[nt] = QS[nt] = zero;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        half8 bs;
-        const _Float16* sp = &sx[buf][16 * nt + nn][32 * j + 4 * gq];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bs[i] = sp[i];
-          bs[i + 4] = sp[16 + i];
-        }
-        X[nt] = mfma_f16(kn[j], bs, X[nt]);
-        QS[nt] = mfma_f16(qb[j], bs, QS[nt]);
-      }
-    }
-    load_kq(rn);
-    // -- Y = V - Kbar S for this wave's rows, all-gathered in fp16
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      half4 hy;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hy[i] = static_cast<_Float16>(X[nt][i] + bf16_bits_to_f32(vraw[nt][i]));
-      *reinterpret_cast<half4*>(&yx[buf][16 * nt + nn][16 * w + 4 * gq]) = hy;
-    }
-    load_v(cn);
-    __syncthreads();
-    // -- U' = M Y, all 64 rows (each wave keeps a full copy), split into fp16 hi + lo
-    half8 uh[NT][2], ul[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      half8 by[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const _Float16* yp = &yx[buf][16 * nt + nn][32 * ks + 4 * gq];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          by[ks][i] = yp[i];
-          by[ks][i + 4] = yp[16 + i];
-        }
-      }
-      floatx4 U[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        U[mt] = mfma_f16(mf[mt][0], by[0], zero);
-        U[mt] = mfma_f16(mf[mt][1], by[1], U[mt]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          _Float16 hh, ll;
-          split_f16(i < 4 ? U[2 * ks][i] : U[2 * ks + 1][i - 4], hh, ll);
-          uh[nt][ks][i] = hh;
-          ul[nt][ks][i] = ll;
-        }
-    }
-    load_m(rn);
-    // -- outputs of this wave's rows: Qbar S + Aqk U' (for rows < 32 the second k-step
-    //    multiplies the zero upper part of Aqk; it is kept so the loop body has no branch)
-    {
-      const rsrc_t ro = make_rsrc(o_base + c * tok_step, rows_bytes(c, (int)sizeof(TOut)));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        floatx4 acc = QS[nt];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          acc = mfma_f16(ahi[ks], uh[nt][ks], acc);
-          acc = mfma_f16(ahi[ks], ul[nt][ks], acc);
-          acc = mfma_f16(alo[ks], uh[nt][ks], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (sizeof(TOut) == 4)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), ro, o_off[nt][i], 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[i]), ro, o_off[nt][i], 0, 0);
-        }
-      }
-    }
-    load_a(rn);
-    // -- this wave's state rows: S = Diag(e^{G_C}) S + Ktil^T U'
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        s[nt][u] *= gam[u];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          s[nt][u] = mfma_f16(kt[u][ks], uh[nt][ks], s[nt][u]);
-          s[nt][u] = mfma_f16(kt[u][ks], ul[nt][ks], s[nt][u]);
-        }
-      }
-    load_kt(rn);
-    buf ^= 1;
-  }
-  if (S_T) {
+    for (int nt = 0; nt < NT; ++nt) col[nt] = 16 * (NT * sg + nt) + nn;
+    // rows 32w + 16u + 4gq + i (u = 0, 1), columns col[nt]
+    floatx4 s[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+          s[nt][u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] : 0.f;
+
+    const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
+    half8 wn[4], kt[2][2];
+    floatx4 ut[NT], gam[2];
+    auto load_w = [&](rsrc_t r) {  // -W of this wave's chunk rows, Utilde tiles
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wn[j] = ld_frag(r, frag_off, OFF_WN + (j * 4 + w) * 1024);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        ut[nt] = ld_tile(r, frag_off, OFF_UT + ((NT * sg + nt) * 4 + w) * 1024);
+    };
+    // e^{G_C} is only used in the update's final fma, which also needs Ktil^T: loaded
+    // together, they share one wait
+    auto load_kt = [&](rsrc_t r) {  // Ktil^T of this wave's key rows, e^{G_C}
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) gam[u] = ld_tile(r, gam_off, 64 * u);
+    };
+    if (nc > 0) {
+      const rsrc_t r0 = make_rsrc(blk_base, (int64_t)kBlockBytes);
+      load_w(r0);
+      load_kt(r0);
+    }
+    // Nothing may be pending on entry to the loop: the compiler computes the loop's memory
+    // waits from the merge of its entry paths and the back edge, and loads left in flight on
+    // an entry path (the conditional ones above) would turn every wait in the loop into a
+    // full one.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int64_t c = 0; c < nc; ++c) {
+      // operands of the next chunk are loaded right after their use in this one (the last
+      // chunk reloads itself), unconditionally and in a fixed order, so every load has a
+      // chunk's time to land and the loop carries no branch
+      const int64_t cn = min(c + 1, nc - 1);
+      const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+      // -- all-gather the state strips in fp16
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          half4 hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
+          *reinterpret_cast<half4*>(&sx[16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
+        }
+      __syncthreads();
+      // -- U' = Utilde - W S for this wave's 16 chunk rows, all-gathered as fp16 hi + lo
+      floatx4 U[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) U[nt] = ut[nt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(wn[j], state_frag(nt, j), U[nt]);
+      load_w(rn);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        half4 hh, ll;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          _Float16 a, bq;
+          split_f16(U[nt][i], a, bq);
+          hh[i] = a;
+          ll[i] = bq;
+        }
+        *reinterpret_cast<half4*>(&ux[0][16 * nt + nn][16 * w + 4 * gq]) = hh;
+        *reinterpret_cast<half4*>(&ux[1][16 * nt + nn][16 * w + 4 * gq]) = ll;
+      }
+      __syncthreads();
+      // -- this wave's state rows: S = Diag(e^{G_C}) S + Ktil^T U'
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        half8 uh[2], ul[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          uh[ks] = lds_frag(&ux[0][16 * nt + nn][32 * ks], gq);
+          ul[ks] = lds_frag(&ux[1][16 * nt + nn][32 * ks], gq);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            acc = mfma_f16(kt[u][ks], uh[ks], acc);
+            acc = mfma_f16(kt[u][ks], ul[ks], acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[nt][u][i] = fmaf(gam[u][i], s[nt][u][i], acc[i]);
+        }
+      }
+      load_kt(rn);
+    }
+    if (S_T) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+    }
+  } else {
+    // ------------------------------------------------ output waves: chunk rows 16w .. 16w+15
+    const int row_stride = H * DV;  // elements between consecutive tokens
+    int o_off[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + 16 * (NT * sg + nt) + nn) * (int)sizeof(TOut);
+    TOut* o_base = o + (si.tok0 * H + h) * DV;
+    const size_t tok_step = (size_t)C * row_stride;
+    half8 qh[4];
+    floatx4 oh[NT];
+    auto load_q = [&](rsrc_t r) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        oh[nt] = ld_tile(r, frag_off, OFF_OH + ((NT * sg + nt) * 4 + w) * 1024);
+    };
+    if (nc > 0) load_q(make_rsrc(blk_base, (int64_t)kBlockBytes));
+    __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
+    for (int64_t c = 0; c < nc; ++c) {
+      const int64_t cn = min(c + 1, nc - 1);
+      const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+      __syncthreads();
+      floatx4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = oh[nt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f16(qh[j], state_frag(nt, j), acc[nt]);
+      load_q(rn);
+      // bytes of the chunk's rows of this head, up to the end of its last valid row
+      const int64_t rows = min((int64_t)C, si.len - c * C);
+      const rsrc_t ro = make_rsrc(o_base + c * tok_step, ((rows - 1) * row_stride + DV) * (int64_t)sizeof(TOut));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (sizeof(TOut) == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[nt][i]), ro, o_off[nt][i], 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[nt][i]), ro, o_off[nt][i], 0, 0);
+        }
+      __syncthreads();
+    }
   }
 }
 
@@ -735,8 +790,9 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   if (prep_blocks > 0)
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
-                       static_cast<const uint16_t*>(p.g), static_cast<const uint16_t*>(p.beta),
-                       p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, ws);
+                       static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.g),
+                       static_cast<const uint16_t*>(p.beta), p.cu_seqlens, chunk_off, p.T, p.H,
+                       p.n_seq, ws);
   const int64_t pairs = (int64_t)p.n_seq * p.H;
   // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
   // workgroup maximises parallelism. Many pairs (at least four strip workgroups per CU): two
@@ -746,24 +802,23 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   const bool two = pairs * NSTRIP >= 4LL * n_cu;
   const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
-  const dim3 grid((unsigned)rec_blocks), block(256);
-  const uint16_t* vv = static_cast<const uint16_t*>(p.v);
+  const dim3 grid((unsigned)rec_blocks), block(512);
   const int64_t mc = max_chunks(p);
   if (p.out_bf16) {
     uint16_t* oo = static_cast<uint16_t*>(p.o);
     if (two)
-      hipLaunchKernelGGL((rec_kernel<uint16_t, 2>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+      hipLaunchKernelGGL((rec_kernel<uint16_t, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
                          p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
     else
-      hipLaunchKernelGGL((rec_kernel<uint16_t, 1>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+      hipLaunchKernelGGL((rec_kernel<uint16_t, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
                          p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
   } else {
     float* oo = static_cast<float*>(p.o);
     if (two)
-      hipLaunchKernelGGL((rec_kernel<float, 2>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+      hipLaunchKernelGGL((rec_kernel<float, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
                          p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
     else
-      hipLaunchKernelGGL((rec_kernel<float, 1>), grid, block, 0, stream, vv, p.S0, oo, p.S_T,
+      hipLaunchKernelGGL((rec_kernel<float, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
                          p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
   }
   return hipGetLastError();
