@@ -590,6 +590,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
 
   if (wave < 4) {
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
+    // they carry the serial chain: when both roles have work ready on a SIMD, theirs issues first
+    __builtin_amdgcn_s_setprio(2);
     const int64_t s_base = pair * DK * DV;
     int col[NT];
 #pragma unroll
@@ -605,41 +607,38 @@ __global__ __launch_bounds__(512) void rec_kernel(
           s[nt][u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] : 0.f;
 
     const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
-    half8 wn[4], kt[2][2];
-    floatx4 ut[NT], gam[2];
-    auto load_w = [&](rsrc_t r) {  // -W of this wave's chunk rows, Utilde tiles
+    // Operands are loaded two chunks ahead into two register sets used alternately (the
+    // loop is unrolled by two, so no set is ever copied): a chunk's loads have two chunks'
+    // time to arrive, which covers a first read of the workspace from HBM.
+    struct Ops {
+      half8 wn[4], kt[2][2];
+      floatx4 ut[NT], gam[2];
+    };
+    Ops A, B;
+    auto load_w = [&](Ops& X, rsrc_t r) {  // -W of this wave's chunk rows, Utilde tiles
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wn[j] = ld_frag(r, frag_off, OFF_WN + (j * 4 + w) * 1024);
+      for (int j = 0; j < 4; ++j) X.wn[j] = ld_frag(r, frag_off, OFF_WN + (j * 4 + w) * 1024);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        ut[nt] = ld_tile(r, frag_off, OFF_UT + ((NT * sg + nt) * 4 + w) * 1024);
+        X.ut[nt] = ld_tile(r, frag_off, OFF_UT + ((NT * sg + nt) * 4 + w) * 1024);
     };
     // e^{G_C} is only used in the update's final fma, which also needs Ktil^T: loaded
     // together, they share one wait
-    auto load_kt = [&](rsrc_t r) {  // Ktil^T of this wave's key rows, e^{G_C}
+    auto load_kt = [&](Ops& X, rsrc_t r) {  // Ktil^T of this wave's key rows, e^{G_C}
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
+        for (int ks = 0; ks < 2; ++ks) X.kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) gam[u] = ld_tile(r, gam_off, 64 * u);
+      for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
     };
-    if (nc > 0) {
-      const rsrc_t r0 = make_rsrc(blk_base, (int64_t)kBlockBytes);
-      load_w(r0);
-      load_kt(r0);
-    }
-    // Nothing may be pending on entry to the loop: the compiler computes the loop's memory
-    // waits from the merge of its entry paths and the back edge, and loads left in flight on
-    // an entry path (the conditional ones above) would turn every wait in the loop into a
-    // full one.
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int64_t c = 0; c < nc; ++c) {
-      // operands of the next chunk are loaded right after their use in this one (the last
-      // chunk reloads itself), unconditionally and in a fixed order, so every load has a
-      // chunk's time to land and the loop carries no branch
-      const int64_t cn = min(c + 1, nc - 1);
-      const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+    auto chunk_rsrc = [&](int64_t c) {
+      return make_rsrc(blk_base + min(c, nc - 1) * blk_step, (int64_t)kBlockBytes);
+    };
+    // one chunk with operand set X; X is then reloaded for chunk c + 2 (past the end, the last
+    // chunk reloads itself), unconditionally and in a fixed order, so the loop has no branch
+    auto step = [&](Ops& X, int64_t c) {
+      const rsrc_t rn = chunk_rsrc(c + 2);
       // -- all-gather the state strips in fp16
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -651,15 +650,18 @@ __global__ __launch_bounds__(512) void rec_kernel(
           *reinterpret_cast<half4*>(&sx[16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
         }
       __syncthreads();
-      // -- U' = Utilde - W S for this wave's 16 chunk rows, all-gathered as fp16 hi + lo
-      floatx4 U[NT];
+      // -- U' = Utilde - W S for this wave's 16 chunk rows, all-gathered as fp16 hi + lo;
+      //    two independent accumulation chains over the four k-steps halve the latency
+      floatx4 U[NT], U2[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) U[nt] = ut[nt];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(wn[j], state_frag(nt, j), U[nt]);
-      load_w(rn);
+      for (int nt = 0; nt < NT; ++nt) {
+        U[nt] = mfma_f16(X.wn[0], state_frag(nt, 0), X.ut[nt]);
+        U2[nt] = mfma_f16(X.wn[2], state_frag(nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
+        U[nt] = mfma_f16(X.wn[1], state_frag(nt, 1), U[nt]);
+        U2[nt] = mfma_f16(X.wn[3], state_frag(nt, 3), U2[nt]);
+        U[nt] += U2[nt];
+      }
+      load_w(X, rn);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         half4 hh, ll;
@@ -683,20 +685,42 @@ __global__ __launch_bounds__(512) void rec_kernel(
           uh[ks] = lds_frag(&ux[0][16 * nt + nn][32 * ks], gq);
           ul[ks] = lds_frag(&ux[1][16 * nt + nn][32 * ks], gq);
         }
+        floatx4 ah[2], al[2];  // hi and lo chains of both row tiles: four independent chains
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            acc = mfma_f16(kt[u][ks], uh[ks], acc);
-            acc = mfma_f16(kt[u][ks], ul[ks], acc);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[nt][u][i] = fmaf(gam[u][i], s[nt][u][i], acc[i]);
+          ah[u] = mfma_f16(X.kt[u][0], uh[0], floatx4{0.f, 0.f, 0.f, 0.f});
+          al[u] = mfma_f16(X.kt[u][0], ul[0], floatx4{0.f, 0.f, 0.f, 0.f});
         }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          ah[u] = mfma_f16(X.kt[u][1], uh[1], ah[u]);
+          al[u] = mfma_f16(X.kt[u][1], ul[1], al[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], ah[u][i] + al[u][i]);
       }
-      load_kt(rn);
+      load_kt(X, rn);
+    };
+    if (nc > 0) {
+      const rsrc_t r0 = chunk_rsrc(0), r1 = chunk_rsrc(1);
+      load_w(A, r0);
+      load_kt(A, r0);
+      load_w(B, r1);
+      load_kt(B, r1);
     }
+    // Nothing may be pending on entry to the loop: the compiler computes the loop's memory
+    // waits from the merge of its entry paths and the back edge, and loads left in flight on
+    // an entry path (the conditional ones above) would turn every wait in the loop into a
+    // full one.
+    __builtin_amdgcn_s_waitcnt(0);
+    int64_t c = 0;
+    for (; c + 1 < nc; c += 2) {
+      step(A, c);
+      step(B, c + 1);
+    }
+    if (c < nc) step(A, c);
     if (S_T) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -717,29 +741,35 @@ __global__ __launch_bounds__(512) void rec_kernel(
         o_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + 16 * (NT * sg + nt) + nn) * (int)sizeof(TOut);
     TOut* o_base = o + (si.tok0 * H + h) * DV;
     const size_t tok_step = (size_t)C * row_stride;
-    half8 qh[4];
-    floatx4 oh[NT];
-    auto load_q = [&](rsrc_t r) {
+    struct Ops {
+      half8 qh[4];
+      floatx4 oh[NT];
+    };
+    Ops A, B;
+    auto load_q = [&](Ops& X, int64_t c) {
+      const rsrc_t r = make_rsrc(blk_base + min(c, nc - 1) * blk_step, (int64_t)kBlockBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
+      for (int j = 0; j < 4; ++j) X.qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        oh[nt] = ld_tile(r, frag_off, OFF_OH + ((NT * sg + nt) * 4 + w) * 1024);
+        X.oh[nt] = ld_tile(r, frag_off, OFF_OH + ((NT * sg + nt) * 4 + w) * 1024);
     };
-    if (nc > 0) load_q(make_rsrc(blk_base, (int64_t)kBlockBytes));
-    __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
-    for (int64_t c = 0; c < nc; ++c) {
-      const int64_t cn = min(c + 1, nc - 1);
-      const rsrc_t rn = make_rsrc(blk_base + cn * blk_step, (int64_t)kBlockBytes);
+    auto step = [&](Ops& X, int64_t c) {
       __syncthreads();
-      floatx4 acc[NT];
+      // the products read the state before the second barrier (the state waves rewrite it
+      // after that barrier); the stores follow it, off the state waves' path
+      floatx4 acc[NT], acc2[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = oh[nt];
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = mfma_f16(X.qh[0], state_frag(nt, 0), X.oh[nt]);
+        acc2[nt] = mfma_f16(X.qh[2], state_frag(nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[nt] = mfma_f16(X.qh[1], state_frag(nt, 1), acc[nt]);
+        acc2[nt] = mfma_f16(X.qh[3], state_frag(nt, 3), acc2[nt]);
+      }
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f16(qh[j], state_frag(nt, j), acc[nt]);
-      load_q(rn);
+      for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
+      load_q(X, c + 2);
       // bytes of the chunk's rows of this head, up to the end of its last valid row
       const int64_t rows = min((int64_t)C, si.len - c * C);
       const rsrc_t ro = make_rsrc(o_base + c * tok_step, ((rows - 1) * row_stride + DV) * (int64_t)sizeof(TOut));
@@ -752,8 +782,18 @@ __global__ __launch_bounds__(512) void rec_kernel(
           else
             __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[nt][i]), ro, o_off[nt][i], 0, 0);
         }
-      __syncthreads();
+    };
+    if (nc > 0) {
+      load_q(A, 0);
+      load_q(B, 1);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
+    int64_t c = 0;
+    for (; c + 1 < nc; c += 2) {
+      step(A, c);
+      step(B, c + 1);
+    }
+    if (c < nc) step(A, c);
   }
 }
 
