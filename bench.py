@@ -212,6 +212,18 @@ def main():
     wall, ms = time_launches(step, args.steps, args.warmup, stream)
     per_ms = sum(ms) / len(ms)
     cold = time_cold(step, args.cold_steps, stream) if args.cold_steps else None
+    # the same launch also storing the state every 512 tokens (sparse checkpoints)
+    ck_every = 512
+    lens = [T] * B if cu is None else list(x.cu_seqlens[1:] - x.cu_seqlens[:-1])
+    ck = torch.empty((binding.checkpoint_slots(lens, ck_every), H, d, d), dtype=torch.float32,
+                     device="cuda")
+
+    def step_ck():
+        binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T, workspace=ws, stream=stream,
+                          ckpt=ck, ckpt_every=ck_every)
+
+    _, ms_ck = time_launches(step_ck, max(10, args.steps // 4), 3, stream)
+    ck_ms = sum(ms_ck) / len(ms_ck)
     token_heads = B * T * H
     flops = flops_per_token_head() * token_heads
     nbytes = bytes_per_token_head() * token_heads + 2 * 4 * d * d * n_seq * H
@@ -240,7 +252,10 @@ def main():
                     "attainable_frac": (flops / (per_ms * 1e-3)) / attainable,
                     "workspace_bytes": nbytes_ws,
                     "cold_event_ms_median": cold and cold[0], "cold_event_ms_min": cold and cold[1],
-                    "cold_steps": args.cold_steps},
+                    "cold_steps": args.cold_steps,
+                    "ckpt": {"every_tokens": ck_every, "slots": ck.shape[0],
+                             "event_ms_per_launch": ck_ms,
+                             "overhead_vs_plain": ck_ms / per_ms - 1.0}},
         "roofline": {"kernel": "kda_chunk_fwd launch (prep_kernel + rec_kernel)", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_GENERIC = 1
+ABI_VERSION = 2  # KDA_ABI_VERSION of include/kda.h this binding marshals for
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_DECAY_RANGE", 6: "KDA_ERR_WORKSPACE",
           7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
@@ -31,7 +32,8 @@ class ChunkArgs(ctypes.Structure):
                 ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
                 ("S0", _P), ("o", _P), ("S_T", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint)]
+                ("flags", ctypes.c_uint),
+                ("ckpt", _P), ("ckpt_every", ctypes.c_int), ("ckpt_slots", ctypes.c_int)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -76,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_abi_version.argtypes = []
         L.kda_abi_version.restype = ctypes.c_int
+        if L.kda_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libkda ABI {L.kda_abi_version()} does not match the binding's "
+                               f"{ABI_VERSION}; rebuild with python -m gated_delta_rule_59_amd.build")
         _lib = L
     return _lib
 
@@ -113,7 +118,7 @@ def _stream(stream) -> _P:
 
 
 def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, S_T=None,
-               workspace=None, generic=False) -> ChunkArgs:
+               workspace=None, generic=False, ckpt=None, ckpt_every=0) -> ChunkArgs:
     B, T, H, dk = q.shape
     a = ChunkArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, v.shape[-1], chunk
@@ -127,7 +132,16 @@ def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, 
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.flags = KDA_FLAG_GENERIC if generic else 0
+    a.ckpt = _ptr(ckpt)
+    a.ckpt_every = ckpt_every
+    a.ckpt_slots = 0 if ckpt is None else ckpt.shape[0]
     return a
+
+
+def checkpoint_slots(lengths, every: int) -> int:
+    """Slots a checkpoint buffer needs for sequences of these lengths: one per full `every`
+    tokens of each sequence (host-side arithmetic, the layout of kda_chunk_args.ckpt)."""
+    return int(sum(int(n) // every for n in lengths)) if every > 0 else 0
 
 
 def chunk_fwd_workspace_bytes(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
@@ -147,11 +161,13 @@ def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
               out_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None,
-              generic=False, stream=None):
+              generic=False, stream=None, ckpt=None, ckpt_every=0):
     """Prefill. q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H] (bf16 or fp32, on the
     GPU, contiguous); S0 [n_seq, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] or None.
     Returns (o [B, T, H, dv] out_dtype, S_T [n_seq, H, dk, dv] fp32 or None).
-    S_T may be passed as S0 itself to continue in place."""
+    S_T may be passed as S0 itself to continue in place.
+    ckpt_every > 0 (a multiple of chunk) also stores the state after every ckpt_every tokens
+    of each sequence into ckpt [slots, H, dk, dv] fp32 (see checkpoint_slots)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     if S0 is not None:
@@ -173,8 +189,15 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
         nbytes = chunk_fwd_workspace_bytes(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk,
                                            generic=generic)
         workspace = alloc_workspace(nbytes, q.device)
+    if ckpt_every:
+        if ckpt is None:
+            raise ValueError("ckpt_every needs a ckpt buffer (size it with checkpoint_slots)")
+        _dev(ckpt, "ckpt")
+        if ckpt.dtype != torch.float32 or tuple(ckpt.shape[1:]) != (H, dk, dv):
+            raise ValueError("ckpt must be fp32 [slots, H, dk, dv]")
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
-                   workspace=workspace, generic=generic)
+                   workspace=workspace, generic=generic, ckpt=ckpt if ckpt_every else None,
+                   ckpt_every=ckpt_every)
     _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
     return o, S_T
 

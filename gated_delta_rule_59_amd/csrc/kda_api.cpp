@@ -100,10 +100,17 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
     return fail(KDA_ERR_BAD_SHAPE, "problem too large");
   if ((int64_t)n_seq * a->H * (a->dv / 16) > 0x7fffffffLL)
     return fail(KDA_ERR_BAD_SHAPE, "too many (sequence, head) pairs");
+  if (a->ckpt_every < 0 || (a->ckpt_every > 0 && a->ckpt_every % a->chunk != 0))
+    return fail(KDA_ERR_BAD_SHAPE, "ckpt_every must be 0 or a positive multiple of chunk (got %d)",
+                a->ckpt_every);
+  if (a->ckpt_every > 0 && a->ckpt_slots < 0)
+    return fail(KDA_ERR_BAD_SHAPE, "ckpt_slots must be >= 0 (got %d)", a->ckpt_slots);
+  const bool ck = a->ckpt_every > 0 && a->ckpt_slots > 0;
   *p = kda::ChunkPlan{a->B, a->T, a->H, a->dk, a->dv, a->chunk, a->cu_seqlens, n_seq,
                       a->act_dtype == KDA_BF16, a->out_dtype == KDA_BF16,
                       a->q, a->k, a->v, a->g, a->beta, a->S0, a->o, a->S_T,
-                      a->workspace, a->workspace_bytes};
+                      a->workspace, a->workspace_bytes,
+                      ck ? a->ckpt : nullptr, ck ? a->ckpt_every : 0, ck ? a->ckpt_slots : 0};
   return KDA_OK;
 }
 
@@ -149,6 +156,11 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
     return fail(KDA_ERR_ALIAS, "S_T overlaps %s", r.name);
   }
   if (overlap(sT, o)) return fail(KDA_ERR_ALIAS, "S_T overlaps o");
+  if (p.ckpt_every > 0 && !a->ckpt) return fail(KDA_ERR_NULL_PTR, "ckpt is NULL with ckpt_every > 0");
+  const Range ck = range("ckpt", p.ckpt, p.ckpt ? (size_t)p.ckpt_slots * a->H * a->dk * a->dv * 4 : 0);
+  for (const Range& r : in)
+    if (overlap(ck, r)) return fail(KDA_ERR_ALIAS, "ckpt overlaps %s", r.name);
+  if (overlap(ck, o) || overlap(ck, sT)) return fail(KDA_ERR_ALIAS, "ckpt overlaps an output");
 
   const bool fast = use_fast(a, p);
   if (fast) {
@@ -161,7 +173,8 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
     const Range ws = range("workspace", a->workspace, need);
     for (const Range& r : in)
       if (overlap(ws, r)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", r.name);
-    if (overlap(ws, o) || overlap(ws, sT)) return fail(KDA_ERR_ALIAS, "workspace overlaps an output");
+    if (overlap(ws, o) || overlap(ws, sT) || overlap(ws, ck))
+      return fail(KDA_ERR_ALIAS, "workspace overlaps an output");
   }
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (env_check()) {

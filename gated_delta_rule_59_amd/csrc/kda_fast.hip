@@ -77,36 +77,48 @@ __device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int3
   return s;
 }
 
-// chunk_off[n] = number of chunks of sequences 0..n-1 (lengths clamped as in seq_info).
+// chunk_off[n] = number of chunks of sequences 0..n-1 (lengths clamped as in seq_info), and,
+// when every > 0, ckpt_off[n] = number of state checkpoints of sequences 0..n-1 (one per full
+// `every` tokens of each).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int n_seq,
-                                                   int T, int32_t* __restrict__ chunk_off) {
-  __shared__ int64_t part[256];
+                                                   int T, int every, int32_t* __restrict__ chunk_off,
+                                                   int32_t* __restrict__ ckpt_off) {
+  __shared__ int64_t part[2][256];
   const int t = threadIdx.x;
   const int per = (n_seq + 255) / 256;
   const int lo = min(t * per, n_seq), hi = min(lo + per, n_seq);
-  int64_t sum = 0;
-  for (int n = lo; n < hi; ++n) {
+  auto seq_len = [&](int n) {
     const int64_t a = min(max((int64_t)cu[n], (int64_t)0), (int64_t)T);
     const int64_t e = min(max((int64_t)cu[n + 1], a), (int64_t)T);
-    sum += (e - a + C - 1) / C;
+    return e - a;
+  };
+  int64_t sum = 0, sck = 0;
+  for (int n = lo; n < hi; ++n) {
+    const int64_t len = seq_len(n);
+    sum += (len + C - 1) / C;
+    if (every > 0) sck += len / every;
   }
-  part[t] = sum;
+  part[0][t] = sum;
+  part[1][t] = sck;
   __syncthreads();
-  if (t == 0) {
+  if (t < 2) {
     int64_t acc = 0;
     for (int i = 0; i < 256; ++i) {
-      const int64_t x = part[i];
-      part[i] = acc;
+      const int64_t x = part[t][i];
+      part[t][i] = acc;
       acc += x;
     }
   }
   __syncthreads();
-  int64_t acc = part[t];
+  int64_t acc = part[0][t], ack = part[1][t];
   for (int n = lo; n < hi; ++n) {
+    const int64_t len = seq_len(n);
     chunk_off[n] = (int32_t)acc;
-    const int64_t a = min(max((int64_t)cu[n], (int64_t)0), (int64_t)T);
-    const int64_t e = min(max((int64_t)cu[n + 1], a), (int64_t)T);
-    acc += (e - a + C - 1) / C;
+    acc += (len + C - 1) / C;
+    if (every > 0) {
+      ckpt_off[n] = (int32_t)ack;
+      ack += len / every;
+    }
   }
   if (t == 255) chunk_off[n_seq] = (int32_t)acc;
 }
@@ -553,7 +565,8 @@ template <typename TOut, int NT>
 __global__ __launch_bounds__(512) void rec_kernel(
     const float* __restrict__ S0, TOut* __restrict__ o, float* __restrict__ S_T,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
-    int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws) {
+    int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws, float* __restrict__ ckpt,
+    int ckpt_chunks, int ckpt_slots, const int32_t* __restrict__ ckpt_off) {
   // A workgroup owns NT strips of 16 value columns. Two fp16 exchanges per chunk through
   // LDS, each followed by a barrier: the state strips (all 128 key rows), which every wave
   // needs whole for W S or Qhat S of its 16 chunk rows, and U' (all 64 chunk rows) for the
@@ -587,6 +600,9 @@ __global__ __launch_bounds__(512) void rec_kernel(
 
   // B operand of state strip nt for key rows 32 j + kslot(gq, i), column nn
   auto state_frag = [&](int nt, int j) { return lds_frag(&sx[16 * nt + nn][32 * j], gq); };
+  // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
+  const int64_t ck_base =
+      ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
 
   if (wave < 4) {
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
@@ -702,6 +718,19 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i) s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], ah[u][i] + al[u][i]);
       }
       load_kt(X, rn);
+      // -- the state after every ckpt_chunks full chunks, if asked for
+      if (ckpt_chunks > 0 && (c + 1) % ckpt_chunks == 0 && (c + 1) * C <= si.len) {
+        const int64_t slot = ck_base + (c + 1) / ckpt_chunks - 1;
+        if (slot < ckpt_slots) {
+          float* dst = ckpt + (slot * H + h) * DK * DV;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dst[(int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+        }
+      }
     };
     if (nc > 0) {
       const rsrc_t r0 = chunk_rsrc(0), r1 = chunk_rsrc(1);
@@ -806,6 +835,9 @@ size_t chunk_table_offset(const ChunkPlan& p) {
   return (size_t)max_chunks(p) * p.H * kBlockBytes;
 }
 
+// packed sequences: chunk offsets, then checkpoint offsets, after the blocks
+size_t table_bytes(const ChunkPlan& p) { return ((sizeof(int32_t) * (p.n_seq + 1) + 255) / 256) * 256; }
+
 }  // namespace
 
 bool fast_path_applies(const ChunkPlan& p) {
@@ -814,18 +846,20 @@ bool fast_path_applies(const ChunkPlan& p) {
 
 size_t fast_workspace_bytes(const ChunkPlan& p) {
   size_t bytes = chunk_table_offset(p);
-  if (p.cu_seqlens) bytes += ((sizeof(int32_t) * (p.n_seq + 1) + 255) / 256) * 256;
+  if (p.cu_seqlens) bytes += 2 * table_bytes(p);
   return bytes;
 }
 
 hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
-  int32_t* chunk_off = nullptr;
+  int32_t *chunk_off = nullptr, *ckpt_off = nullptr;
   if (p.cu_seqlens) {
     chunk_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p));
+    ckpt_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p) + table_bytes(p));
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seq, p.T,
-                       chunk_off);
+                       p.ckpt ? p.ckpt_every : 0, chunk_off, ckpt_off);
   }
+  const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
   const int64_t prep_blocks = max_chunks(p) * p.H;
   if (prep_blocks > 0)
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream,
@@ -848,18 +882,22 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     uint16_t* oo = static_cast<uint16_t*>(p.o);
     if (two)
       hipLaunchKernelGGL((rec_kernel<uint16_t, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
+                         ck_chunks, p.ckpt_slots, ckpt_off);
     else
       hipLaunchKernelGGL((rec_kernel<uint16_t, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
+                         ck_chunks, p.ckpt_slots, ckpt_off);
   } else {
     float* oo = static_cast<float*>(p.o);
     if (two)
       hipLaunchKernelGGL((rec_kernel<float, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
+                         ck_chunks, p.ckpt_slots, ckpt_off);
     else
       hipLaunchKernelGGL((rec_kernel<float, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws);
+                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
+                         ck_chunks, p.ckpt_slots, ckpt_off);
   }
   return hipGetLastError();
 }

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void chunk_generic_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, const float* __restrict__ S0,
     TOut* __restrict__ o, float* __restrict__ S_T, const int32_t* __restrict__ cu_seqlens,
-    int T, int H, int dk, int dv, int C, int n_seq) {
+    int T, int H, int dk, int dv, int C, int n_seq, float* __restrict__ ckpt, int ckpt_every,
+    int ckpt_slots) {
   extern __shared__ float lds[];
   const GenericLds L = generic_lds(C, dk);
   float* Ks = lds + L.off_k;
@@ -81,6 +82,20 @@ __global__ __launch_bounds__(256) void chunk_generic_kernel(
   } else {
     tok0 = (int64_t)n * T;
     len = T;
+  }
+  // first checkpoint slot of this sequence: one checkpoint per full ckpt_every tokens of
+  // each earlier sequence
+  int64_t ck_base = 0;
+  if (ckpt) {
+    if (cu_seqlens) {
+      for (int m = 0; m < n; ++m) {  // lengths clamped as above
+        const int64_t a = min(max((int64_t)cu_seqlens[m], (int64_t)0), (int64_t)T);
+        const int64_t e = min(max((int64_t)cu_seqlens[m + 1], a), (int64_t)T);
+        ck_base += (e - a) / ckpt_every;
+      }
+    } else {
+      ck_base = (int64_t)n * (T / ckpt_every);
+    }
   }
 
   const int64_t s_base = ((int64_t)n * H + h) * dk * dv;
@@ -177,6 +192,15 @@ __global__ __launch_bounds__(256) void chunk_generic_kernel(
         acc += Ks[r * dk + c] * __expf(gC - Gs[r * dk + c]) * Us[r * kDVS + j];
       Ss[i] = acc;
     }
+    // the state after every ckpt_every full tokens (each thread stores the entries it owns)
+    if (ckpt && (t0 + C) % ckpt_every == 0 && t0 + C <= len) {
+      const int64_t slot = ck_base + (t0 + C) / ckpt_every - 1;
+      if (slot < ckpt_slots) {
+        float* dst = ckpt + (slot * H + h) * dk * dv;
+        for (int i = tid; i < dk * kDVS; i += 256)
+          dst[(int64_t)(i / kDVS) * dv + col0 + i % kDVS] = Ss[i];
+      }
+    }
   }
   __syncthreads();
   if (S_T) {
@@ -199,7 +223,8 @@ hipError_t launch_generic_t(const ChunkPlan& p, hipStream_t stream) {
                      static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
                      static_cast<const TIn*>(p.v), static_cast<const TIn*>(p.g),
                      static_cast<const TIn*>(p.beta), p.S0, static_cast<TOut*>(p.o), p.S_T,
-                     p.cu_seqlens, p.T, p.H, p.dk, p.dv, p.chunk, p.n_seq);
+                     p.cu_seqlens, p.T, p.H, p.dk, p.dv, p.chunk, p.n_seq, p.ckpt, p.ckpt_every,
+                     p.ckpt_slots);
   return hipGetLastError();
 }
 

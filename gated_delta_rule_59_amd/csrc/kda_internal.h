@@ -27,6 +27,9 @@ struct ChunkPlan {
   float* S_T;
   void* workspace;
   size_t workspace_bytes;
+  float* ckpt;      // state checkpoints [ckpt_slots, H, dk, dv], or nullptr
+  int ckpt_every;   // tokens between checkpoints (a multiple of chunk), 0 = none
+  int ckpt_slots;
 };
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -91,6 +91,20 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *              when that is 0), 256-byte aligned; contents on entry are ignored.
  *   flags      0, or KDA_FLAG_GENERIC to force the fp32 vector-ALU path (needs no
  *              workspace; slower; used to cross-check the matrix-core path).
+ *   ckpt, ckpt_every, ckpt_slots
+ *              Sparse state checkpoints for prefix reuse: the fixed-size state is the whole
+ *              memory of a prefix, so a later request that shares the prefix can resume from
+ *              a stored state instead of recomputing it (orkas.ai Kimi K3 page, the
+ *              serving-infrastructure section on per-request state). ckpt_every = 0 writes
+ *              none (ckpt and ckpt_slots are then ignored). Otherwise ckpt_every is a positive
+ *              multiple of chunk, and ckpt is fp32 [ckpt_slots, H, dk, dv]: checkpoint j >= 1
+ *              of sequence n is its state after its first j * ckpt_every tokens (for every j
+ *              with j * ckpt_every <= len_n), stored in slot
+ *                  sum_{m < n} floor(len_m / ckpt_every) + j - 1.
+ *              Slots at or past ckpt_slots are not written (a caller that allocates
+ *              sum_n floor(len_n / ckpt_every) slots gets every checkpoint; that sum is at
+ *              most floor(B * T / ckpt_every)). ckpt must not overlap any input, o, S_T or
+ *              the workspace.
  */
 typedef struct {
     int B, T, H, dk, dv, chunk;
@@ -104,6 +118,9 @@ typedef struct {
     void* workspace;
     size_t workspace_bytes;
     unsigned flags;
+    float* ckpt;
+    int ckpt_every;
+    int ckpt_slots;
 } kda_chunk_args;
 
 #define KDA_FLAG_GENERIC 1u

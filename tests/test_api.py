@@ -33,7 +33,7 @@ def test_exports_every_declared_function(b):
                           "kda_abi_version"}
     for n in names:
         assert hasattr(b.lib(), n), n
-    assert b.lib().kda_abi_version() == 1
+    assert b.lib().kda_abi_version() == b.ABI_VERSION == 2
 
 
 def test_status_strings(b):
@@ -91,6 +91,24 @@ def test_chunk_varlen_rules(b):
     assert call_chunk(b, a)[0] == 2
     a = base_args(b, cu_seqlens=FAKE + (1 << 32), N=3, B=2)
     assert call_chunk(b, a)[0] == 2
+
+
+def test_chunk_checkpoint_rules(b):
+    """ckpt_every must be a multiple of the chunk length; a buffer is then required and
+    must not overlap anything else; ckpt_every = 0 ignores the other two fields."""
+    flags = b.KDA_FLAG_GENERIC   # no workspace needed, so validation reaches the ckpt rules
+    ck = FAKE + (1 << 33)
+    assert call_chunk(b, base_args(b, flags=flags, ckpt=ck, ckpt_every=96, ckpt_slots=4))[0] == 2
+    assert call_chunk(b, base_args(b, flags=flags, ckpt=ck, ckpt_every=-64, ckpt_slots=4))[0] == 2
+    assert call_chunk(b, base_args(b, flags=flags, ckpt=ck, ckpt_every=128, ckpt_slots=-1))[0] == 2
+    assert call_chunk(b, base_args(b, flags=flags, ckpt=None, ckpt_every=128, ckpt_slots=4))[0] == 1
+    a = base_args(b, flags=flags, ckpt_every=128, ckpt_slots=2)
+    a.ckpt = a.k   # on top of an input
+    rc, msg = call_chunk(b, a)
+    assert rc == 8 and "ckpt overlaps k" in msg
+    a = base_args(b, flags=flags, ckpt_every=128, ckpt_slots=2)
+    a.ckpt = a.o + 64
+    assert call_chunk(b, a)[0] == 8
 
 
 def test_workspace_query(b):
