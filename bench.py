@@ -145,6 +145,25 @@ def bench_decode(steps, warmup, stream):
     wall, ms = time_launches(step, steps, warmup, stream)
     per = sum(ms) / len(ms)
     nbytes = N * H * (2 * 4 * d * d + 2 * (4 * d + 1) + 4 * d)  # state in+out, inputs, fp32 o
+
+    # speculative decoding on the same state: 4 draft tokens per sequence evaluated from one
+    # read of S (verify, S untouched), then all 4 committed (S read and written, no outputs)
+    m = 4
+    drafts = [torch.from_numpy(a).cuda().to(torch.bfloat16)
+              for a in inputs.draw_activations((0, 4, 1000), N, m, H, d, d, "bf16")]
+    o_m = torch.empty((N, m, H, d), dtype=torch.float32, device="cuda")
+    acc = torch.full((N,), m, dtype=torch.int32, device="cuda")
+    n_sp = max(10, steps // 4)
+    _, ms_v = time_launches(lambda: binding.decode_multi(*drafts, S, o=o_m, stream=stream),
+                            n_sp, 3, stream)
+    _, ms_c = time_launches(lambda: binding.decode_multi(*drafts, S, accept=acc,
+                                                         want_output=False, stream=stream),
+                            n_sp, 3, stream)
+    v_ms, c_ms = sum(ms_v) / len(ms_v), sum(ms_c) / len(ms_c)
+    in_b = N * m * H * 2 * (4 * d + 1)
+    spec = {"m": m, "verify_ms": v_ms, "verify_tokens_per_s": N * m / (v_ms * 1e-3),
+            "verify_GB_per_s": (N * H * 4 * d * d + in_b + N * m * H * 4 * d) / (v_ms * 1e-3) / 1e9,
+            "commit_ms": c_ms, "commit_GB_per_s": (N * H * 8 * d * d + in_b) / (c_ms * 1e-3) / 1e9}
     ksrc = os.path.join(ROOT, "gated_delta_rule_59_amd", "csrc", "kda_decode.hip")
     traffic = read_traffic("decode-512_decode_step_kernel_traffic.txt", src_hash(ksrc))
     gbs = nbytes / (per * 1e-3) / 1e9
@@ -152,7 +171,7 @@ def bench_decode(steps, warmup, stream):
                         "fp32 o)",
             "steps": steps, "warmup": warmup, "ms_per_step": per,
             "wall_ms_per_step": wall * 1e3 / steps,
-            "tokens_per_s": N / (per * 1e-3), "GB_per_s": gbs,
+            "tokens_per_s": N / (per * 1e-3), "GB_per_s": gbs, "spec_decode": spec,
             "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": traffic}}

@@ -45,6 +45,15 @@ class DecodeArgs(ctypes.Structure):
                 ("S", _P), ("o", _P)]
 
 
+class DecodeMultiArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("m", ctypes.c_int),
+                ("act_dtype", ctypes.c_int), ("gate_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
+                ("S", _P), ("o", _P), ("accept", _P)]
+
+
 class KDAError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -69,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.kda_decode_step.restype = ctypes.c_int
+        L.kda_decode_multi.argtypes = [ctypes.POINTER(DecodeMultiArgs), _P]
+        L.kda_decode_multi.restype = ctypes.c_int
         L.kda_check_gates.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int, _P,
                                       ctypes.POINTER(ctypes.c_int64)]
         L.kda_check_gates.restype = ctypes.c_int
@@ -222,6 +233,34 @@ def decode_step(q, k, v, g, beta, S, *, o=None, out_dtype=torch.float32, stream=
         o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=out_dtype, device=q.device)
     a = decode_args(q, k, v, g, beta, S, o)
     _check(lib().kda_decode_step(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def decode_multi(q, k, v, g, beta, S, *, accept=None, o=None, want_output=True,
+                 out_dtype=torch.float32, stream=None):
+    """m tokens per sequence from one read of S: q, k, g [N, m, H, dk]; v [N, m, H, dv];
+    beta [N, m, H]; S [N, H, dk, dv] fp32. accept None: S unchanged (verification);
+    accept int32 [N] on the GPU: S[n] <- state after its first accept[n] tokens (commit).
+    Returns o [N, m, H, dv] (None when want_output is False and o is not given)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S", S)):
+        _dev(t, name)
+    N, m, H, dk = q.shape
+    if accept is not None:
+        _dev(accept, "accept")
+        if accept.dtype != torch.int32 or accept.numel() != N:
+            raise ValueError("accept must be int32 [N]")
+    if o is None and want_output:
+        o = torch.empty((N, m, H, v.shape[-1]), dtype=out_dtype, device=q.device)
+    elif o is not None:
+        _dev(o, "o")
+    a = DecodeMultiArgs()
+    a.N, a.H, a.dk, a.dv, a.m = N, H, dk, v.shape[-1], m
+    a.act_dtype = _dtype_code(q.dtype)
+    a.gate_dtype = _dtype_code(g.dtype)
+    a.out_dtype = _dtype_code(o.dtype) if o is not None else KDA_F32
+    a.q, a.k, a.v, a.g, a.beta, a.S = (_ptr(t) for t in (q, k, v, g, beta, S))
+    a.o, a.accept = _ptr(o), _ptr(accept)
+    _check(lib().kda_decode_multi(ctypes.byref(a), _stream(stream)))
     return o
 
 

@@ -229,6 +229,50 @@ kda_status kda_decode_step(const kda_decode_args* a, void* hip_stream) {
   return ok();
 }
 
+kda_status kda_decode_multi(const kda_decode_multi_args* a, void* hip_stream) {
+  if (!a) return fail(KDA_ERR_NULL_PTR, "args is NULL");
+  if (a->N < 1 || a->H < 1 || a->m < 1)
+    return fail(KDA_ERR_BAD_SHAPE, "need N, H, m >= 1 (got N=%d H=%d m=%d)", a->N, a->H, a->m);
+  if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv))
+    return fail(KDA_ERR_BAD_SHAPE, "dk and dv must be 32, 64 or 128 (got %d, %d)", a->dk, a->dv);
+  if ((int64_t)a->N * a->H > 0x7fffffffLL || (int64_t)a->N * a->m * a->H > (int64_t(1) << 40))
+    return fail(KDA_ERR_BAD_SHAPE, "N * m * H too large");
+  if (!dtype_ok(a->act_dtype) || !dtype_ok(a->gate_dtype) || !dtype_ok(a->out_dtype))
+    return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
+  if (a->act_dtype != a->gate_dtype)
+    return fail(KDA_ERR_BAD_DTYPE, "act_dtype and gate_dtype must match (both F32 or both BF16)");
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->S)
+    return fail(KDA_ERR_NULL_PTR, "q, k, v, g, beta and S must be non-NULL");
+  const size_t es = dsize(a->act_dtype), os = dsize(a->out_dtype);
+  const size_t nh = (size_t)a->N * a->H, nmh = nh * a->m;
+  const Range in[] = {range("q", a->q, nmh * a->dk * es), range("k", a->k, nmh * a->dk * es),
+                      range("v", a->v, nmh * a->dv * es), range("g", a->g, nmh * a->dk * es),
+                      range("beta", a->beta, nmh * es),
+                      range("accept", a->accept, a->accept ? sizeof(int32_t) * a->N : 0)};
+  const Range S = range("S", a->S, nh * a->dk * a->dv * 4);
+  const Range o = range("o", a->o, a->o ? nmh * a->dv * os : 0);
+  for (const Range& r : in) {
+    if (overlap(o, r)) return fail(KDA_ERR_ALIAS, "o overlaps %s", r.name);
+    if (overlap(S, r)) return fail(KDA_ERR_ALIAS, "S overlaps %s", r.name);
+  }
+  if (overlap(S, o)) return fail(KDA_ERR_ALIAS, "S overlaps o");
+  if (!a->o && !a->accept) return ok();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (env_check()) {
+    int64_t bad = 0;
+    kda_status s = run_gate_check(a->g, (int64_t)(nmh * a->dk), a->beta, (int64_t)nmh,
+                                  a->gate_dtype, stream, &bad);
+    if (s != KDA_OK) return s;
+    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
+  }
+  const kda::DecodeMultiPlan p{a->N, a->H, a->dk, a->dv, a->m, a->act_dtype == KDA_BF16,
+                               a->out_dtype == KDA_BF16, a->q, a->k, a->v, a->g, a->beta,
+                               a->S, a->o, a->accept};
+  const hipError_t e = kda::launch_decode_multi(p, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_decode_multi launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 kda_status kda_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
                            kda_dtype gate_dtype, void* hip_stream, int64_t* n_bad) {
   if (!n_bad) return fail(KDA_ERR_NULL_PTR, "n_bad is NULL");

@@ -34,6 +34,17 @@ struct ChunkPlan {
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 
+struct DecodeMultiPlan {
+  int N, H, dk, dv, m;
+  bool act_bf16, out_bf16;
+  const void *q, *k, *v, *g, *beta;
+  float* S;
+  void* o;                // nullptr: outputs not written
+  const int32_t* accept;  // nullptr: S not modified
+};
+
+hipError_t launch_decode_multi(const DecodeMultiPlan& p, hipStream_t stream);
+
 // Generic path: fp32 arithmetic on the vector ALUs, any supported dk/dv/chunk; used for
 // fp32 activations and for shapes the matrix-core path does not take.
 hipError_t launch_chunk_generic(const ChunkPlan& p, hipStream_t stream);

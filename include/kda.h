@@ -138,6 +138,29 @@ typedef struct {
     void* o;
 } kda_decode_args;
 
+/* Arguments of kda_decode_multi: m tokens for each of N independent sequences, evaluated
+ * from one read of the state. It serves speculative decoding, which must evaluate draft
+ * tokens without committing them and then commit the accepted prefix (orkas.ai Kimi K3
+ * page, serving-infrastructure section on speculative decoding and in-place state).
+ *   m       tokens per sequence, >= 1.
+ *   q, k, g [N, m, H, dk];  v [N, m, H, dv];  beta [N, m, H]: token j of sequence n at [n, j].
+ *   S       [N, H, dk, dv] fp32. Token j sees the state after tokens 0..j-1 of its sequence.
+ *   o       [N, m, H, dv] out_dtype, every token's output (read after its update); or NULL.
+ *   accept  device int32 [N], or NULL. NULL: S is left unchanged (verification). Otherwise
+ *           S[n] becomes the state after the first clamp(accept[n], 0, m) tokens (commit;
+ *           0 leaves S[n] unchanged). A verify call followed by a commit call with the same
+ *           inputs replays the accepted tokens; o of the two calls agree bitwise.
+ *   Inputs and accept must not overlap S or o; S and o must not overlap.
+ */
+typedef struct {
+    int N, H, dk, dv, m;
+    kda_dtype act_dtype, gate_dtype, out_dtype;
+    const void *q, *k, *v, *g, *beta;
+    float* S;
+    void* o;
+    const int32_t* accept;
+} kda_decode_multi_args;
+
 /* Bytes of device workspace kda_chunk_fwd needs for these arguments (pointers are not
  * inspected). Writes 0 to *bytes when the chosen path needs none. Validates shapes and
  * dtypes like kda_chunk_fwd. */
@@ -148,6 +171,10 @@ kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
 
 /* Decode: one step for every (sequence, head); S updated in place, o written. */
 kda_status kda_decode_step(const kda_decode_args* args, void* hip_stream);
+
+/* Decode, m tokens per sequence: outputs of all m, and optionally the commit of an accepted
+ * prefix into S (see kda_decode_multi_args). With o and accept both NULL nothing is done. */
+kda_status kda_decode_multi(const kda_decode_multi_args* args, void* hip_stream);
 
 /* Device check of the preconditions on the gates: counts g values outside [-5, 0] and
  * beta values outside [0, 1] (NaN counts as outside). n_g, n_beta elements; dtype of both

@@ -147,6 +147,32 @@ def test_decode_rejects_bad_args(b):
     assert b.lib().kda_decode_step(None, None) == 1
 
 
+def test_decode_multi_rejects_bad_args(b):
+    a = b.DecodeMultiArgs()
+    a.N, a.H, a.dk, a.dv, a.m = 4, 2, 128, 128, 3
+    a.act_dtype = a.gate_dtype = b.KDA_BF16
+    a.out_dtype = b.KDA_F32
+    a.q, a.k, a.v, a.g, a.beta = (FAKE + i * (1 << 20) for i in range(5))
+    a.S = FAKE + (1 << 30)
+    a.o = FAKE + (1 << 31)
+    call = lambda: b.lib().kda_decode_multi(ctypes.byref(a), None)  # noqa: E731
+    a.m = 0
+    assert call() == 2
+    a.m = 3
+    a.S = None
+    assert call() == 1
+    a.S = FAKE + (1 << 30)
+    a.o = a.S + 64   # inside the state
+    assert call() == 8
+    a.o = FAKE + (1 << 31)
+    a.accept = a.S   # the accepted counts on top of the state
+    assert call() == 8
+    a.accept = None
+    a.o = None       # nothing asked for: a no-op, accepted without touching the device
+    assert call() == 0
+    assert b.lib().kda_decode_multi(None, None) == 1
+
+
 def test_check_gates_rejects_bad_args(b):
     n = ctypes.c_int64(0)
     assert b.lib().kda_check_gates(None, 10, None, 0, 1, None, ctypes.byref(n)) == 1
