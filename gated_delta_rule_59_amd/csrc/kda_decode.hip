@@ -19,8 +19,12 @@
 
 namespace kda {
 
+// At least 7 waves per SIMD (at most 72 VGPRs): more workgroups in flight per CU keep more
+// of the state stream in flight. Measured on the 1 GiB decode workload: 0.378 ms per step,
+// against 0.407 ms at the 95 VGPRs the compiler picks unconstrained and 0.390 ms at 6 waves;
+// the 128 x 128 state then spills a few VGPRs, which costs less than the lost occupancy.
 template <int DK, int DV, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(256, 7) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ S,
     TOut* __restrict__ o, int64_t n_heads_total) {
@@ -106,8 +110,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // accept, S[n] becomes the state after the first clamp(accept[n], 0, m) tokens. The state
 // stays in registers across the tokens: one read of S, and one write only when committing.
 // Same thread layout as decode_step_kernel; inputs are [N, m, H, d].
+// At least 4 waves per SIMD (128 VGPRs): verification of 4 drafts on the 1 GiB decode state
+// takes 0.264 ms against 0.296 ms at the 140 VGPRs the compiler picks unconstrained.
 template <int DK, int DV, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void decode_multi_kernel(
+__global__ __launch_bounds__(256, 4) void decode_multi_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ S,
     TOut* __restrict__ o, const int32_t* __restrict__ accept, int H, int m,
