@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
-    int n_seq, uint8_t* __restrict__ ws) {
+    int n_seq, uint8_t* __restrict__ ws, int c_lo, int c_span) {
   constexpr int TR = C + 8;         // row stride (fp16) of the channel-major staging arrays
   constexpr int AS = C + 4;         // row stride (fp32) of A and T
   constexpr int STG = DK * TR * 2;  // bytes of one staging array
@@ -214,16 +214,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     }
     n = lo;
     c_in = cid - chunk_off[n];
-  } else {
+  } else {  // dense batch: chunks c_lo .. c_lo + c_span - 1 of every sequence
     const int64_t ncs = (T + C - 1) / C;
-    n = (int)(cid / ncs);
-    c_in = cid % ncs;
-    if (n >= n_seq) return;
+    n = (int)(cid / c_span);
+    c_in = c_lo + cid % c_span;
+    if (n >= n_seq || c_in >= ncs) return;
   }
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   const int64_t tok0 = si.tok0 + c_in * C;
   const int Cn = (int)min((int64_t)C, si.len - c_in * C);
-  uint8_t* blk = ws + ((size_t)cid * H + h) * kBlockBytes;
+  uint8_t* blk = ws + ((size_t)(si.cid0 + c_in) * H + h) * kBlockBytes;
 
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -566,7 +566,11 @@ __global__ __launch_bounds__(512) void rec_kernel(
     const float* __restrict__ S0, TOut* __restrict__ o, float* __restrict__ S_T,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
     int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws, float* __restrict__ ckpt,
-    int ckpt_chunks, int ckpt_slots, const int32_t* __restrict__ ckpt_off) {
+    int ckpt_chunks, int ckpt_slots, const int32_t* __restrict__ ckpt_off, int64_t c_lo,
+    int64_t c_hi) {
+  // Walks chunks c_lo .. c_hi - 1 of each sequence (those that exist), entering with the state
+  // S0 (zeros if null) and leaving it in S_T (not written if null); chunk indices, and with
+  // them the workspace blocks, checkpoints and outputs, are the sequence's own.
   // A workgroup owns NT strips of 16 value columns. Two fp16 exchanges per chunk through
   // LDS, each followed by a barrier: the state strips (all 128 key rows), which every wave
   // needs whole for W S or Qhat S of its 16 chunk rows, and U' (all 64 chunk rows) for the
@@ -589,6 +593,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   // a malformed cu_seqlens cannot make the chunk walk leave the workspace
   const int64_t nc = max((int64_t)0, min((si.len + C - 1) / C, max_chunks - si.cid0));
+  const int64_t c_end = min(nc, c_hi);  // this launch walks chunks c_lo .. c_end - 1
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
       for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
     };
     auto chunk_rsrc = [&](int64_t c) {
-      return make_rsrc(blk_base + min(c, nc - 1) * blk_step, (int64_t)kBlockBytes);
+      return make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)kBlockBytes);
     };
     // one chunk with operand set X; X is then reloaded for chunk c + 2 (past the end, the last
     // chunk reloads itself), unconditionally and in a fixed order, so the loop has no branch
@@ -732,8 +737,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
         }
       }
     };
-    if (nc > 0) {
-      const rsrc_t r0 = chunk_rsrc(0), r1 = chunk_rsrc(1);
+    if (c_end > c_lo) {
+      const rsrc_t r0 = chunk_rsrc(c_lo), r1 = chunk_rsrc(c_lo + 1);
       load_w(A, r0);
       load_kt(A, r0);
       load_w(B, r1);
@@ -744,12 +749,12 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // an entry path (the conditional ones above) would turn every wait in the loop into a
     // full one.
     __builtin_amdgcn_s_waitcnt(0);
-    int64_t c = 0;
-    for (; c + 1 < nc; c += 2) {
+    int64_t c = c_lo;
+    for (; c + 1 < c_end; c += 2) {
       step(A, c);
       step(B, c + 1);
     }
-    if (c < nc) step(A, c);
+    if (c < c_end) step(A, c);
     if (S_T) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -776,7 +781,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
     };
     Ops A, B;
     auto load_q = [&](Ops& X, int64_t c) {
-      const rsrc_t r = make_rsrc(blk_base + min(c, nc - 1) * blk_step, (int64_t)kBlockBytes);
+      const rsrc_t r = make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)kBlockBytes);
 #pragma unroll
       for (int j = 0; j < 4; ++j) X.qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
 #pragma unroll
@@ -812,17 +817,17 @@ __global__ __launch_bounds__(512) void rec_kernel(
             __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[nt][i]), ro, o_off[nt][i], 0, 0);
         }
     };
-    if (nc > 0) {
-      load_q(A, 0);
-      load_q(B, 1);
+    if (c_end > c_lo) {
+      load_q(A, c_lo);
+      load_q(B, c_lo + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
-    int64_t c = 0;
-    for (; c + 1 < nc; c += 2) {
+    int64_t c = c_lo;
+    for (; c + 1 < c_end; c += 2) {
       step(A, c);
       step(B, c + 1);
     }
-    if (c < nc) step(A, c);
+    if (c < c_end) step(A, c);
   }
 }
 
@@ -850,6 +855,36 @@ size_t fast_workspace_bytes(const ChunkPlan& p) {
   return bytes;
 }
 
+namespace {
+
+template <typename TOut>
+hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int64_t pairs,
+                      const float* S_in, float* S_out, int64_t c_lo, int64_t c_hi,
+                      const int32_t* chunk_off, const int32_t* ckpt_off, uint8_t* ws) {
+  const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
+  const dim3 grid((unsigned)rec_blocks), block(512);
+  const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
+  auto kern = two ? rec_kernel<TOut, 2> : rec_kernel<TOut, 1>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, S_in, static_cast<TOut*>(p.o), S_out,
+                     p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws, p.ckpt,
+                     ck_chunks, p.ckpt_slots, ckpt_off, c_lo, c_hi);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* chunk_off,
+                       uint8_t* ws, int c_lo, int c_span) {
+  const int64_t blocks = p.cu_seqlens ? max_chunks(p) * p.H : (int64_t)p.n_seq * c_span * p.H;
+  if (blocks > 0)
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                       static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.g),
+                       static_cast<const uint16_t*>(p.beta), p.cu_seqlens, chunk_off, p.T, p.H,
+                       p.n_seq, ws, c_lo, c_span);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
   int32_t *chunk_off = nullptr, *ckpt_off = nullptr;
@@ -859,47 +894,20 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seq, p.T,
                        p.ckpt ? p.ckpt_every : 0, chunk_off, ckpt_off);
   }
-  const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
-  const int64_t prep_blocks = max_chunks(p) * p.H;
-  if (prep_blocks > 0)
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
-                       static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.g),
-                       static_cast<const uint16_t*>(p.beta), p.cu_seqlens, chunk_off, p.T, p.H,
-                       p.n_seq, ws);
   const int64_t pairs = (int64_t)p.n_seq * p.H;
-  // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
-  // workgroup maximises parallelism. Many pairs (at least four strip workgroups per CU): two
-  // strips per workgroup halve the operand traffic per column.
+  const int ncs = (int)((p.T + C - 1) / C);
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
+  // workgroup maximises parallelism. Many pairs (at least four strip workgroups per CU): two
+  // strips per workgroup halve the operand traffic per column.
   const bool two = pairs * NSTRIP >= 4LL * n_cu;
-  const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
-  const dim3 grid((unsigned)rec_blocks), block(512);
-  const int64_t mc = max_chunks(p);
-  if (p.out_bf16) {
-    uint16_t* oo = static_cast<uint16_t*>(p.o);
-    if (two)
-      hipLaunchKernelGGL((rec_kernel<uint16_t, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
-                         ck_chunks, p.ckpt_slots, ckpt_off);
-    else
-      hipLaunchKernelGGL((rec_kernel<uint16_t, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
-                         ck_chunks, p.ckpt_slots, ckpt_off);
-  } else {
-    float* oo = static_cast<float*>(p.o);
-    if (two)
-      hipLaunchKernelGGL((rec_kernel<float, 2>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
-                         ck_chunks, p.ckpt_slots, ckpt_off);
-    else
-      hipLaunchKernelGGL((rec_kernel<float, 1>), grid, block, 0, stream, p.S0, oo, p.S_T,
-                         p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, mc, ws, p.ckpt,
-                         ck_chunks, p.ckpt_slots, ckpt_off);
-  }
-  return hipGetLastError();
+  hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
+  if (e != hipSuccess) return e;
+  return p.out_bf16
+             ? launch_rec<uint16_t>(p, stream, two, pairs, p.S0, p.S_T, 0, INT64_MAX, chunk_off, ckpt_off, ws)
+             : launch_rec<float>(p, stream, two, pairs, p.S0, p.S_T, 0, INT64_MAX, chunk_off, ckpt_off, ws);
 }
 
 }  // namespace kda

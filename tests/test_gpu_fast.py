@@ -30,6 +30,13 @@ def dense_batch_case():
     return inputs.KDAInputs(wl, q, k, v, g, beta, S0)
 
 
+def batch_case(B, T, H):
+    q, k, v, g, beta = inputs.draw_activations((9, 6, B, T, H), B, T, H, 128, 128, "bf16")
+    S0 = inputs.draw_state((9, 6, B, T, H), B, H, 128, 128)
+    wl = inputs.Workload("batch", 1, H, 128, 128, 64, "bf16", B=B, T=T)
+    return inputs.KDAInputs(wl, q, k, v, g, beta, S0)
+
+
 CASES = {
     "prefill-4k T=300 H=2": lambda: inputs.make_prefill(1, T=300, H=2),
     "prefill-64k-bound T=1024 H=4": lambda: inputs.make_prefill(2, T=1024, H=4),
@@ -38,6 +45,8 @@ CASES = {
     "ragged varlen H=32 (two strips per workgroup)": lambda: ragged_case(H=32),
     "dense batch B=3 T=130": dense_batch_case,
     "no initial state": lambda: _no_s0(inputs.make_prefill(1, T=200, H=2)),
+    "dense batch B=2 T=1093 H=3 (18 chunks, partial last)": lambda: batch_case(2, 1093, 3),
+    "no initial state, 9 full chunks": lambda: _no_s0(batch_case(1, 9 * 64, 2)),
 }
 
 
@@ -80,6 +89,22 @@ def test_fast_deterministic_and_in_place():
     import torch
     from gated_delta_rule_59_amd import binding
     x = inputs.make_prefill(1, T=400, H=4)
+    q, k, v, g, beta, S0, _ = kda_inputs_dev(x)
+    o1, s1 = binding.chunk_fwd(q, k, v, g, beta, S0)
+    o2, s2 = binding.chunk_fwd(q, k, v, g, beta, S0)
+    S = S0.clone()
+    o3, _ = binding.chunk_fwd(q, k, v, g, beta, S, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, S)
+
+
+def test_batch_in_place_and_deterministic():
+    """A two-sequence batch with a partial last chunk continues in place (S_T = S0) and
+    repeats bitwise."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    x = batch_case(2, 1093, 3)
     q, k, v, g, beta, S0, _ = kda_inputs_dev(x)
     o1, s1 = binding.chunk_fwd(q, k, v, g, beta, S0)
     o2, s2 = binding.chunk_fwd(q, k, v, g, beta, S0)
