@@ -243,6 +243,13 @@ def main():
 
     _, ms_ck = time_launches(step_ck, max(10, args.steps // 4), 3, stream)
     ck_ms = sum(ms_ck) / len(ms_ck)
+    # ablation: the same launch with the diagonal tiles evaluated pairwise (what the decay
+    # bound's dense diagonal tiles save)
+    _, ms_pw = time_launches(lambda: binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T,
+                                                       workspace=ws, stream=stream,
+                                                       pairwise_diag=True),
+                             max(10, args.steps // 4), 3, stream)
+    pw_ms = sum(ms_pw) / len(ms_pw)
     token_heads = B * T * H
     flops = flops_per_token_head() * token_heads
     nbytes = bytes_per_token_head() * token_heads + 2 * 4 * d * d * n_seq * H
@@ -274,7 +281,9 @@ def main():
                     "cold_steps": args.cold_steps,
                     "ckpt": {"every_tokens": ck_every, "slots": ck.shape[0],
                              "event_ms_per_launch": ck_ms,
-                             "overhead_vs_plain": ck_ms / per_ms - 1.0}},
+                             "overhead_vs_plain": ck_ms / per_ms - 1.0},
+                    "pairwise_diag_ablation": {"event_ms_per_launch": pw_ms,
+                                               "slowdown_vs_dense_diag": pw_ms / per_ms}},
         "roofline": {"kernel": "kda_chunk_fwd launch (prep_kernel + rec_kernel)", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_GENERIC = 1
+KDA_FLAG_PAIRWISE_DIAG = 2
 ABI_VERSION = 2  # KDA_ABI_VERSION of include/kda.h this binding marshals for
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_DECAY_RANGE", 6: "KDA_ERR_WORKSPACE",
@@ -129,7 +130,8 @@ def _stream(stream) -> _P:
 
 
 def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, S_T=None,
-               workspace=None, generic=False, ckpt=None, ckpt_every=0) -> ChunkArgs:
+               workspace=None, generic=False, ckpt=None, ckpt_every=0,
+               pairwise_diag=False) -> ChunkArgs:
     B, T, H, dk = q.shape
     a = ChunkArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, v.shape[-1], chunk
@@ -142,7 +144,7 @@ def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, 
     a.S0, a.o, a.S_T = _ptr(S0), _ptr(o), _ptr(S_T)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a.flags = KDA_FLAG_GENERIC if generic else 0
+    a.flags = (KDA_FLAG_GENERIC if generic else 0) | (KDA_FLAG_PAIRWISE_DIAG if pairwise_diag else 0)
     a.ckpt = _ptr(ckpt)
     a.ckpt_every = ckpt_every
     a.ckpt_slots = 0 if ckpt is None else ckpt.shape[0]
@@ -172,13 +174,14 @@ def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
               out_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None,
-              generic=False, stream=None, ckpt=None, ckpt_every=0):
+              generic=False, stream=None, ckpt=None, ckpt_every=0, pairwise_diag=False):
     """Prefill. q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H] (bf16 or fp32, on the
     GPU, contiguous); S0 [n_seq, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] or None.
     Returns (o [B, T, H, dv] out_dtype, S_T [n_seq, H, dk, dv] fp32 or None).
     S_T may be passed as S0 itself to continue in place.
     ckpt_every > 0 (a multiple of chunk) also stores the state after every ckpt_every tokens
-    of each sequence into ckpt [slots, H, dk, dv] fp32 (see checkpoint_slots)."""
+    of each sequence into ckpt [slots, H, dk, dv] fp32 (see checkpoint_slots).
+    pairwise_diag evaluates the diagonal tiles pairwise (no lower bound on g needed; slower)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     if S0 is not None:
@@ -208,7 +211,7 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
             raise ValueError("ckpt must be fp32 [slots, H, dk, dv]")
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
                    workspace=workspace, generic=generic, ckpt=ckpt if ckpt_every else None,
-                   ckpt_every=ckpt_every)
+                   ckpt_every=ckpt_every, pairwise_diag=pairwise_diag)
     _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
     return o, S_T
 

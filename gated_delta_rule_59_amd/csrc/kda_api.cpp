@@ -93,7 +93,8 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
     return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
   if (a->act_dtype != a->gate_dtype)
     return fail(KDA_ERR_BAD_DTYPE, "act_dtype and gate_dtype must match (both F32 or both BF16)");
-  if (a->flags & ~KDA_FLAG_GENERIC) return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags);
+  if (a->flags & ~(KDA_FLAG_GENERIC | KDA_FLAG_PAIRWISE_DIAG))
+    return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags);
   const int64_t tokens = (int64_t)a->B * a->T;
   const int n_seq = a->cu_seqlens ? a->N : a->B;
   if (tokens * a->H * (int64_t)(a->dk > a->dv ? a->dk : a->dv) > (int64_t(1) << 40))
@@ -110,7 +111,8 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
                       a->act_dtype == KDA_BF16, a->out_dtype == KDA_BF16,
                       a->q, a->k, a->v, a->g, a->beta, a->S0, a->o, a->S_T,
                       a->workspace, a->workspace_bytes,
-                      ck ? a->ckpt : nullptr, ck ? a->ckpt_every : 0, ck ? a->ckpt_slots : 0};
+                      ck ? a->ckpt : nullptr, ck ? a->ckpt_every : 0, ck ? a->ckpt_slots : 0,
+                      (a->flags & KDA_FLAG_PAIRWISE_DIAG) != 0};
   return KDA_OK;
 }
 

@@ -172,6 +172,10 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 // in the lane layout the next product or the workspace needs: a result tile computed as
 // (column operand) x (row operand) leaves each lane with four entries of its own row, which
 // for two adjacent tiles is exactly an A-operand fragment of that row.
+// PAIRWISE replaces the dense diagonal tiles by the pairwise evaluation of the earlier
+// generation (each e^{G_r - G_j} formed per pair and channel, in fp32 on the vector ALUs),
+// which needs no bound on the decay: the ablation that measures what the bound buys.
+template <bool PAIRWISE>
 __global__ __launch_bounds__(256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
@@ -187,7 +191,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   //   inverse:  A fp32 [64][AS] [0, 17408), T [17408, 34816), scratch [34816, 37888)
   //   products: V^T staging [0, 18432), once M is in registers
   //   last:     W^T [0, 18432), Utilde^T hi [18432, 36864), lo [36864, 55296)
-  __shared__ __align__(16) unsigned char arena[61440];
+  // pairwise tiles stage per wave G fp32 [16][132] and k, q bf16 [16][136] first
+  constexpr int PW_G = 16 * 132 * 4, PW_KQ = 16 * 136 * 2, PW_WAVE = PW_G + 2 * PW_KQ;
+  __shared__ __align__(16) unsigned char arena[PAIRWISE ? 4 * PW_WAVE : 61440];
   __shared__ __align__(16) float TOT[4][DK], PCH[4][DK], ECH[4][DK], XCH[3][DK];
   __shared__ __align__(16) float Bs[C];
   float* KC = reinterpret_cast<float*>(arena);
@@ -289,6 +295,48 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     }
   }
   __syncthreads();
+  // ---- pairwise diagonal tile (ablation): lane (row n = m, columns 4 gq + i) forms
+  //      A[r][j] = sum_c k_r k_j e^{G_r - G_j} and Aqk[r][j] over its four columns j <= r
+  floatx4 pw_k = {0.f, 0.f, 0.f, 0.f}, pw_q = pw_k;
+  if constexpr (PAIRWISE) {
+    float* Gw = reinterpret_cast<float*>(arena + w * PW_WAVE);
+    uint16_t* Kw = reinterpret_cast<uint16_t*>(arena + w * PW_WAVE + PW_G);
+    uint16_t* Qw = reinterpret_cast<uint16_t*>(arena + w * PW_WAVE + PW_G + PW_KQ);
+    const u16x4 zero4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = 32 * ks + 16 * hf + 4 * gq;
+        *reinterpret_cast<floatx4*>(&Gw[m * 132 + c0]) =
+            floatx4{gs[ks][4 * hf], gs[ks][4 * hf + 1], gs[ks][4 * hf + 2], gs[ks][4 * hf + 3]};
+        *reinterpret_cast<u16x4*>(&Kw[m * 136 + c0]) = row_ok ? kraw[ks][hf] : zero4;
+        *reinterpret_cast<u16x4*>(&Qw[m * 136 + c0]) = row_ok ? qraw[ks][hf] : zero4;
+      }
+    __syncthreads();
+    for (int c = 0; c < DK; c += 4) {
+      const floatx4 gr = *reinterpret_cast<const floatx4*>(&Gw[m * 132 + c]);
+      const u16x4 kr4 = *reinterpret_cast<const u16x4*>(&Kw[m * 136 + c]);
+      const u16x4 qr4 = *reinterpret_cast<const u16x4*>(&Qw[m * 136 + c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * gq + i;
+        const floatx4 gj = *reinterpret_cast<const floatx4*>(&Gw[j * 132 + c]);
+        const u16x4 kj4 = *reinterpret_cast<const u16x4*>(&Kw[j * 136 + c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // G_r - G_j <= 0 for j <= r; for j > r the term is discarded below
+          const float f = bf16_bits_to_f32(kj4[e]) * exp2f(fminf(gr[e] - gj[e], 0.f));
+          pw_k[i] = fmaf(bf16_bits_to_f32(kr4[e]), f, pw_k[i]);
+          pw_q[i] = fmaf(bf16_bits_to_f32(qr4[e]), f, pw_q[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * gq + i > m) pw_k[i] = pw_q[i] = 0.f;
+    __syncthreads();  // the arena is reused below
+  }
   // ---- per-element factors and operands
   float kr[4][8], qr[4][8], kd[4][8];  // k rf, q rf, k / rf
   half8 qbar[4];                       // Qbar as A-operand fragments of row tile w
@@ -339,7 +387,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   //      operand), i.e. transposed, so lane l ends with entries (16w + l&15, 16bb + 4 gq + i).
   floatx4 akk[4], aqk[4];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) akk[bb] = aqk[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int bb = 0; bb < 4; ++bb) {
+    akk[bb] = bb == w ? pw_k : floatx4{0.f, 0.f, 0.f, 0.f};
+    aqk[bb] = bb == w ? pw_q : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     half8 rk16, rq16;
@@ -354,12 +405,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       split_bf16(kd[ks][i], hh, ll); ch[i] = hh; cl[i] = ll;
     }
     // diagonal tile: column factor up to e^80, split bf16
-    akk[w] = mfma_bf16(ch, rkh, akk[w]);
-    akk[w] = mfma_bf16(ch, rkl, akk[w]);
-    akk[w] = mfma_bf16(cl, rkh, akk[w]);
-    aqk[w] = mfma_bf16(ch, rqh, aqk[w]);
-    aqk[w] = mfma_bf16(ch, rql, aqk[w]);
-    aqk[w] = mfma_bf16(cl, rqh, aqk[w]);
+    if constexpr (!PAIRWISE) {
+      akk[w] = mfma_bf16(ch, rkh, akk[w]);
+      akk[w] = mfma_bf16(ch, rkl, akk[w]);
+      akk[w] = mfma_bf16(cl, rkh, akk[w]);
+      aqk[w] = mfma_bf16(ch, rqh, aqk[w]);
+      aqk[w] = mfma_bf16(ch, rql, aqk[w]);
+      aqk[w] = mfma_bf16(cl, rqh, aqk[w]);
+    }
     // earlier tiles: factors <= 1, fp16
 #pragma unroll
     for (int bb = 0; bb < 3; ++bb) {
@@ -875,7 +928,8 @@ hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* ch
                        uint8_t* ws, int c_lo, int c_span) {
   const int64_t blocks = p.cu_seqlens ? max_chunks(p) * p.H : (int64_t)p.n_seq * c_span * p.H;
   if (blocks > 0)
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(p.pairwise_diag ? prep_kernel<true> : prep_kernel<false>,
+                       dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                        static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.g),
                        static_cast<const uint16_t*>(p.beta), p.cu_seqlens, chunk_off, p.T, p.H,

@@ -30,6 +30,7 @@ struct ChunkPlan {
   float* ckpt;      // state checkpoints [ckpt_slots, H, dk, dv], or nullptr
   int ckpt_every;   // tokens between checkpoints (a multiple of chunk), 0 = none
   int ckpt_slots;
+  bool pairwise_diag;  // matrix-core path: diagonal tiles pairwise (no decay bound needed)
 };
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);

@@ -125,15 +125,16 @@ def _sigmoid(x):
     return np.float32(1.0) / (np.float32(1.0) + np.exp(-x))
 
 
-def draw_activations(key, B, T, H, dk, dv, dtype):
-    """q, k unit rows over dk; v ~ N(0,1); beta = sigmoid(N(0,1)); g = -5 sigmoid(N(0,1)).
+def draw_activations(key, B, T, H, dk, dv, dtype, gate_floor=GATE_FLOOR):
+    """q, k unit rows over dk; v ~ N(0,1); beta = sigmoid(N(0,1)); g = gate_floor sigmoid(N(0,1))
+    (gate_floor -5 everywhere except the unbounded-decay ablation inputs).
     Shapes [B, T, H, d] ([B, T, H] for beta); drawn over the flattened B*T token axis."""
     n = B * T
     q = _draw(key, 1, (n, H, dk), _unit_rows, dtype).reshape(B, T, H, dk)
     k = _draw(key, 2, (n, H, dk), _unit_rows, dtype).reshape(B, T, H, dk)
     v = _draw(key, 3, (n, H, dv), lambda x: x, dtype).reshape(B, T, H, dv)
     beta = _draw(key, 4, (n, H), _sigmoid, dtype).reshape(B, T, H)
-    g = _draw(key, 5, (n, H, dk), lambda x: np.float32(GATE_FLOOR) * _sigmoid(x),
+    g = _draw(key, 5, (n, H, dk), lambda x: np.float32(gate_floor) * _sigmoid(x),
               dtype).reshape(B, T, H, dk)
     return q, k, v, g, beta
 
@@ -200,3 +201,17 @@ def make_decode_step(p: int, N: int = 512, H: int = 32, dk: int = 128, dv: int =
     in bf16 values, drawn as for prefill-4k. Step s of a run uses set s % DECODE_POOL."""
     q, k, v, g, beta = draw_activations((0, 4, 1 + p), N, 1, H, dk, dv, "bf16")
     return q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0]
+
+
+UNBOUNDED_FLOOR = -20.0    # the ablation's per-step log-decay floor (the -5 bound removed)
+
+
+def make_unbounded(T: int = 4096, H: int = 16, B: int = 1) -> KDAInputs:
+    """prefill-4k's shapes and distributions with g = -20 sigmoid(N(0,1)): per-step decay down
+    to e^-20, so a 16-token tile's cumulative log-decay reaches -320 and the dense diagonal-tile
+    factorisation would need factors up to e^320 (the pairwise-diagonal ablation's inputs)."""
+    key = (0, 5)
+    q, k, v, g, beta = draw_activations(key, B, T, H, 128, 128, "bf16", gate_floor=UNBOUNDED_FLOOR)
+    S0 = draw_state(key, B, H, 128, 128)
+    wl = Workload("unbounded-4k", 5, H, 128, 128, 64, "bf16", B=B, T=T, n_seq=B)
+    return KDAInputs(wl, q, k, v, g, beta, S0)

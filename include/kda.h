@@ -89,8 +89,15 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *              (continue in place); must not partially overlap it.
  *   workspace  device scratch of at least kda_chunk_fwd_workspace() bytes (may be NULL
  *              when that is 0), 256-byte aligned; contents on entry are ignored.
- *   flags      0, or KDA_FLAG_GENERIC to force the fp32 vector-ALU path (needs no
- *              workspace; slower; used to cross-check the matrix-core path).
+ *   flags      0, or any of:
+ *              KDA_FLAG_GENERIC to force the fp32 vector-ALU path (needs no workspace; slower;
+ *              used to cross-check the matrix-core path);
+ *              KDA_FLAG_PAIRWISE_DIAG to evaluate the diagonal 16-token tiles of the
+ *              matrix-core path pairwise (each e^{G_r - G_j} per pair and key channel, fp32, on
+ *              the vector ALUs) as the earlier generation did, instead of by the dense product
+ *              that the decay bound makes possible (orkas.ai Kimi K3 page, "Eine Untergrenze, die
+ *              einen GPU-Codepfad beseitigte"). It needs no lower bound on g (any g <= 0) and is
+ *              slower: the ablation of that bound. (KDA_CHECK=1 still checks g >= -5.)
  *   ckpt, ckpt_every, ckpt_slots
  *              Sparse state checkpoints for prefix reuse: the fixed-size state is the whole
  *              memory of a prefix, so a later request that shares the prefix can resume from
@@ -124,6 +131,7 @@ typedef struct {
 } kda_chunk_args;
 
 #define KDA_FLAG_GENERIC 1u
+#define KDA_FLAG_PAIRWISE_DIAG 2u
 
 /* Arguments of kda_decode_step: one token for each of N independent sequences.
  *   q, k, g [N, H, dk];  v [N, H, dv];  beta [N, H]   (act_dtype / gate_dtype as above)

@@ -333,3 +333,14 @@ def test_state_size_independent_of_length():
         x = inputs.make_prefill(1, T=T, H=2)
         _, s = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0)
         assert s.shape == (1, 2, 128, 128)
+
+
+def test_unbounded_inputs_break_the_tile_bound():
+    """The ablation's inputs (g down to -20) leave the (-80, 0) tile range that the generated
+    workloads respect, so they exercise exactly what the bound rules out."""
+    from gated_delta_rule_59_amd import inputs
+    x = inputs.make_unbounded(T=256, H=2)
+    g = x.g.astype(np.float64)
+    assert g.max() <= 0.0 and g.min() < -5.0
+    tiles = g[0].reshape(16, 16, 2, 128).sum(axis=1)     # 16-token tile sums per channel
+    assert tiles.min() < -80.0
