@@ -128,6 +128,30 @@ def cpu_baseline(x, budget_s=10.0):
                       f"(sequence, head) chains over {threads} OpenMP threads), {el:.1f} s"}
 
 
+def bench_segments(stream, warmup, steps=10):
+    """The segmented walk on the shape it serves: one 65,536-token sequence with 2 heads
+    (prefill-64k-bound's distributions), sequential and in 4 and 8 segments."""
+    import torch
+    from gated_delta_rule_59_amd import binding, inputs
+    x = inputs.make_prefill(2, H=2)
+    dv = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)  # noqa: E731
+    q, k, v, g, beta = (dv(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    S0 = torch.from_numpy(x.S0).cuda()
+    o = torch.empty(q.shape[:3] + (128,), dtype=torch.float32, device="cuda")
+    S_T = torch.empty_like(S0)
+    out = {"workload": "B=1 H=2 T=65536 dk=dv=128, decay floor on half the channels"}
+    for P in (0, 4, 8):
+        ws = binding.alloc_workspace(binding.chunk_fwd_workspace_bytes(q, k, v, g, beta, S0,
+                                                                       segments=P), q.device)
+        _, ms = time_launches(lambda: binding.chunk_fwd(q, k, v, g, beta, S0, o=o, S_T=S_T,
+                                                        workspace=ws, stream=stream,
+                                                        segments=P), steps, max(2, warmup // 4),
+                              stream)
+        out[f"segments_{P}_event_ms" if P else "sequential_event_ms"] = sum(ms) / len(ms)
+    out["tokens_per_s_best"] = 65536 / (min(v for kk, v in out.items() if kk.endswith("_ms")) * 1e-3)
+    return out
+
+
 def bench_decode(steps, warmup, stream):
     import torch
     from gated_delta_rule_59_amd import binding, inputs
@@ -187,6 +211,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra launches timed after a 512 MiB cache flush each (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-segments", action="store_true",
+                    help="skip the segmented-walk timing on the long two-head sequence")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -288,6 +314,8 @@ def main():
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
     }
+    if not args.no_segments:
+        res["segments"] = bench_segments(stream, args.warmup)
     if not args.no_decode:
         res["decode"] = bench_decode(args.decode_steps, max(3, args.warmup // 4), stream)
     if not args.no_cpu:

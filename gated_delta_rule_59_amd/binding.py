@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_GENERIC = 1
 KDA_FLAG_PAIRWISE_DIAG = 2
-ABI_VERSION = 2  # KDA_ABI_VERSION of include/kda.h this binding marshals for
+ABI_VERSION = 3  # KDA_ABI_VERSION of include/kda.h this binding marshals for
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_DECAY_RANGE", 6: "KDA_ERR_WORKSPACE",
           7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
@@ -34,7 +34,8 @@ class ChunkArgs(ctypes.Structure):
                 ("S0", _P), ("o", _P), ("S_T", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
                 ("flags", ctypes.c_uint),
-                ("ckpt", _P), ("ckpt_every", ctypes.c_int), ("ckpt_slots", ctypes.c_int)]
+                ("ckpt", _P), ("ckpt_every", ctypes.c_int), ("ckpt_slots", ctypes.c_int),
+                ("segments", ctypes.c_int)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -131,7 +132,7 @@ def _stream(stream) -> _P:
 
 def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, S_T=None,
                workspace=None, generic=False, ckpt=None, ckpt_every=0,
-               pairwise_diag=False) -> ChunkArgs:
+               pairwise_diag=False, segments=0) -> ChunkArgs:
     B, T, H, dk = q.shape
     a = ChunkArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, v.shape[-1], chunk
@@ -148,6 +149,7 @@ def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, 
     a.ckpt = _ptr(ckpt)
     a.ckpt_every = ckpt_every
     a.ckpt_slots = 0 if ckpt is None else ckpt.shape[0]
+    a.segments = segments
     return a
 
 
@@ -158,8 +160,9 @@ def checkpoint_slots(lengths, every: int) -> int:
 
 
 def chunk_fwd_workspace_bytes(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
-                              generic=False) -> int:
-    a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, generic=generic)
+                              generic=False, segments=0) -> int:
+    a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, generic=generic,
+                   segments=segments)
     n = ctypes.c_size_t(0)
     _check(lib().kda_chunk_fwd_workspace(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
@@ -174,14 +177,16 @@ def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
               out_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None,
-              generic=False, stream=None, ckpt=None, ckpt_every=0, pairwise_diag=False):
+              generic=False, stream=None, ckpt=None, ckpt_every=0, pairwise_diag=False,
+              segments=0):
     """Prefill. q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H] (bf16 or fp32, on the
     GPU, contiguous); S0 [n_seq, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] or None.
     Returns (o [B, T, H, dv] out_dtype, S_T [n_seq, H, dk, dv] fp32 or None).
     S_T may be passed as S0 itself to continue in place.
     ckpt_every > 0 (a multiple of chunk) also stores the state after every ckpt_every tokens
     of each sequence into ckpt [slots, H, dk, dv] fp32 (see checkpoint_slots).
-    pairwise_diag evaluates the diagonal tiles pairwise (no lower bound on g needed; slower)."""
+    pairwise_diag evaluates the diagonal tiles pairwise (no lower bound on g needed; slower).
+    segments (3 .. 8) walks each sequence in that many segments in parallel (see kda.h)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     if S0 is not None:
@@ -201,7 +206,7 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
         S_T = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         nbytes = chunk_fwd_workspace_bytes(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk,
-                                           generic=generic)
+                                           generic=generic, segments=segments)
         workspace = alloc_workspace(nbytes, q.device)
     if ckpt_every:
         if ckpt is None:
@@ -211,7 +216,7 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
             raise ValueError("ckpt must be fp32 [slots, H, dk, dv]")
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
                    workspace=workspace, generic=generic, ckpt=ckpt if ckpt_every else None,
-                   ckpt_every=ckpt_every, pairwise_diag=pairwise_diag)
+                   ckpt_every=ckpt_every, pairwise_diag=pairwise_diag, segments=segments)
     _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
     return o, S_T
 

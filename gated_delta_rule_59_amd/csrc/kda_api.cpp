@@ -106,13 +106,15 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
                 a->ckpt_every);
   if (a->ckpt_every > 0 && a->ckpt_slots < 0)
     return fail(KDA_ERR_BAD_SHAPE, "ckpt_slots must be >= 0 (got %d)", a->ckpt_slots);
+  if (a->segments < 0 || a->segments > 8)
+    return fail(KDA_ERR_BAD_SHAPE, "segments must be in 0 .. 8 (got %d)", a->segments);
   const bool ck = a->ckpt_every > 0 && a->ckpt_slots > 0;
   *p = kda::ChunkPlan{a->B, a->T, a->H, a->dk, a->dv, a->chunk, a->cu_seqlens, n_seq,
                       a->act_dtype == KDA_BF16, a->out_dtype == KDA_BF16,
                       a->q, a->k, a->v, a->g, a->beta, a->S0, a->o, a->S_T,
                       a->workspace, a->workspace_bytes,
                       ck ? a->ckpt : nullptr, ck ? a->ckpt_every : 0, ck ? a->ckpt_slots : 0,
-                      (a->flags & KDA_FLAG_PAIRWISE_DIAG) != 0};
+                      (a->flags & KDA_FLAG_PAIRWISE_DIAG) != 0, a->segments};
   return KDA_OK;
 }
 

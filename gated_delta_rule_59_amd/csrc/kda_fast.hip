@@ -614,16 +614,34 @@ __device__ __forceinline__ floatx4 ld_tile(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
 
+// One walk of the recurrence over chunks c_lo .. c_hi - 1 of every sequence (those that exist;
+// chunk indices, and with them the workspace blocks, checkpoints and outputs, are the
+// sequence's own), for every (sequence, head):
+//   REC_OUTPUT      from S_in (zeros if null): outputs and checkpoints written;
+//   REC_SUMMARY     from zeros, nothing but the exit state: the segment's zero-start summary Z;
+//   REC_TRANSITION  from the identity with V = 0 (Utilde = 0), nothing but the exit state:
+//                   the segment's transition Phi, so that S_exit = Phi S_entry + Z.
+// The exit state goes to S_out when it is not null.
+enum { REC_OUTPUT = 0, REC_SUMMARY = 1, REC_TRANSITION = 2 };
+struct RecJob {
+  int64_t c_lo, c_hi;
+  const float* S_in;
+  float* S_out;
+  int mode;
+};
+constexpr int kMaxJobs = 16;
+struct RecJobs {
+  RecJob job[kMaxJobs];
+  int64_t blocks_per_job;
+};
+
 template <typename TOut, int NT>
 __global__ __launch_bounds__(512) void rec_kernel(
-    const float* __restrict__ S0, TOut* __restrict__ o, float* __restrict__ S_T,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
-    int n_seq, int64_t max_chunks, const uint8_t* __restrict__ ws, float* __restrict__ ckpt,
-    int ckpt_chunks, int ckpt_slots, const int32_t* __restrict__ ckpt_off, int64_t c_lo,
-    int64_t c_hi) {
-  // Walks chunks c_lo .. c_hi - 1 of each sequence (those that exist), entering with the state
-  // S0 (zeros if null) and leaving it in S_T (not written if null); chunk indices, and with
-  // them the workspace blocks, checkpoints and outputs, are the sequence's own.
+    RecJobs jobs, TOut* __restrict__ o, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, int T, int H, int n_seq, int64_t max_chunks,
+    const uint8_t* __restrict__ ws, float* __restrict__ ckpt, int ckpt_chunks, int ckpt_slots,
+    const int32_t* __restrict__ ckpt_off) {
+  // blockIdx.x = job * blocks_per_job + (block within the job)
   // A workgroup owns NT strips of 16 value columns. Two fp16 exchanges per chunk through
   // LDS, each followed by a barrier: the state strips (all 128 key rows), which every wave
   // needs whole for W S or Qhat S of its 16 chunk rows, and U' (all 64 chunk rows) for the
@@ -636,8 +654,13 @@ __global__ __launch_bounds__(512) void rec_kernel(
   __shared__ __align__(16) _Float16 sx[NT * 16][SR];
   __shared__ __align__(16) _Float16 ux[2][NT * 16][UR];
 
+  const RecJob job = jobs.job[blockIdx.x / jobs.blocks_per_job];
+  const int64_t c_lo = job.c_lo, c_hi = job.c_hi;
+  const float* __restrict__ S0 = job.mode == REC_OUTPUT ? job.S_in : nullptr;
+  float* __restrict__ S_T = job.S_out;
+  const bool transition = job.mode == REC_TRANSITION;
   // XCD-aware placement: the strip groups of one (sequence, head) share an XCD and its L2.
-  const int b = blockIdx.x;
+  const int b = (int)(blockIdx.x % jobs.blocks_per_job);
   const int xcd = b & 7, rest = b >> 3;
   const int sg = rest % NG;
   const int64_t pair = (int64_t)(rest / NG) * 8 + xcd;
@@ -661,6 +684,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
   const int64_t ck_base =
       ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
+  const int ck_every = job.mode == REC_OUTPUT ? ckpt_chunks : 0;
 
   if (wave < 4) {
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
@@ -677,8 +701,11 @@ __global__ __launch_bounds__(512) void rec_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[nt][u][i] = S0 ? S0[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 32 * w + 16 * u + 4 * gq + i;
+          s[nt][u][i] = transition ? (r == col[nt] ? 1.f : 0.f)
+                                   : (S0 ? S0[s_base + (int64_t)r * DV + col[nt]] : 0.f);
+        }
 
     const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
     // Operands are loaded two chunks ahead into two register sets used alternately (the
@@ -729,7 +756,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
       floatx4 U[NT], U2[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        U[nt] = mfma_f16(X.wn[0], state_frag(nt, 0), X.ut[nt]);
+        U[nt] = mfma_f16(X.wn[0], state_frag(nt, 0), transition ? floatx4{0.f, 0.f, 0.f, 0.f} : X.ut[nt]);
         U2[nt] = mfma_f16(X.wn[2], state_frag(nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
         U[nt] = mfma_f16(X.wn[1], state_frag(nt, 1), U[nt]);
         U2[nt] = mfma_f16(X.wn[3], state_frag(nt, 3), U2[nt]);
@@ -777,8 +804,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
       }
       load_kt(X, rn);
       // -- the state after every ckpt_chunks full chunks, if asked for
-      if (ckpt_chunks > 0 && (c + 1) % ckpt_chunks == 0 && (c + 1) * C <= si.len) {
-        const int64_t slot = ck_base + (c + 1) / ckpt_chunks - 1;
+      if (ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * C <= si.len) {
+        const int64_t slot = ck_base + (c + 1) / ck_every - 1;
         if (slot < ckpt_slots) {
           float* dst = ckpt + (slot * H + h) * DK * DV;
 #pragma unroll
@@ -816,6 +843,12 @@ __global__ __launch_bounds__(512) void rec_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+    }
+  } else if (job.mode != REC_OUTPUT) {
+    // ------------------------------------------------ no outputs: keep the barriers in step
+    for (int64_t c = c_lo; c < c_end; ++c) {
+      __syncthreads();
+      __syncthreads();
     }
   } else {
     // ------------------------------------------------ output waves: chunk rows 16w .. 16w+15
@@ -884,6 +917,42 @@ __global__ __launch_bounds__(512) void rec_kernel(
   }
 }
 
+// Entry state of the next segment from the previous one's: S_next = Phi S_in + Z, per
+// (sequence, head), fp32. One workgroup per (sequence, head, 16-column strip); Phi is streamed
+// through LDS in 32-column slabs.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Phi,
+                                                      const float* __restrict__ S_in,
+                                                      const float* __restrict__ Z,
+                                                      float* __restrict__ S_next, int64_t pairs) {
+  const int64_t pair = blockIdx.x / NSTRIP;
+  const int strip = blockIdx.x % NSTRIP;
+  if (pair >= pairs) return;
+  __shared__ float sin_s[DK][17];   // S_in strip, [key row][column]
+  __shared__ float phi_s[DK][33];   // Phi rows, one 32-column slab at a time
+  const int t = threadIdx.x;
+  const int64_t base = pair * DK * DV;
+  for (int i = t; i < DK * 16; i += 256)
+    sin_s[i / 16][i % 16] = S_in[base + (int64_t)(i / 16) * DV + 16 * strip + i % 16];
+  const int j = t & 15, r0 = (t >> 4) * 8;  // this thread: rows r0 .. r0 + 7 of column j
+  float acc[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) acc[rr] = Z[base + (int64_t)(r0 + rr) * DV + 16 * strip + j];
+  for (int kb = 0; kb < DK; kb += 32) {
+    __syncthreads();
+    for (int i = t; i < DK * 32; i += 256)
+      phi_s[i / 32][i % 32] = Phi[base + (int64_t)(i / 32) * DK + kb + i % 32];
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      const float sv = sin_s[kb + kk][j];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) acc[rr] = fmaf(phi_s[r0 + rr][kk], sv, acc[rr]);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) S_next[base + (int64_t)(r0 + rr) * DV + 16 * strip + j] = acc[rr];
+}
+
 int64_t max_chunks(const ChunkPlan& p) {
   const int64_t per = (p.T + C - 1) / C;
   return p.cu_seqlens ? per + p.n_seq : (int64_t)p.B * per;
@@ -902,25 +971,33 @@ bool fast_path_applies(const ChunkPlan& p) {
   return p.act_bf16 && p.dk == DK && p.dv == DV && p.chunk == C;
 }
 
+namespace {
+// Segmented walk: P - 1 entry states, and P - 2 summaries and transitions, after the tables.
+int n_segments(const ChunkPlan& p) { return p.segments >= 3 ? p.segments : 1; }
+size_t state_bytes(const ChunkPlan& p) { return (size_t)p.n_seq * p.H * DK * DV * sizeof(float); }
+size_t segment_buffers_offset(const ChunkPlan& p) {
+  return chunk_table_offset(p) + (p.cu_seqlens ? 2 * table_bytes(p) : 0);
+}
+}  // namespace
+
 size_t fast_workspace_bytes(const ChunkPlan& p) {
-  size_t bytes = chunk_table_offset(p);
-  if (p.cu_seqlens) bytes += 2 * table_bytes(p);
-  return bytes;
+  const int P = n_segments(p);
+  return segment_buffers_offset(p) + (P > 1 ? (size_t)(3 * P - 5) * state_bytes(p) : 0);
 }
 
 namespace {
 
 template <typename TOut>
 hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int64_t pairs,
-                      const float* S_in, float* S_out, int64_t c_lo, int64_t c_hi,
-                      const int32_t* chunk_off, const int32_t* ckpt_off, uint8_t* ws) {
-  const int64_t rec_blocks = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
-  const dim3 grid((unsigned)rec_blocks), block(512);
+                      RecJobs jobs, int n_jobs, const int32_t* chunk_off,
+                      const int32_t* ckpt_off, uint8_t* ws) {
+  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
+  const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
   const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
   auto kern = two ? rec_kernel<TOut, 2> : rec_kernel<TOut, 1>;
-  hipLaunchKernelGGL(kern, grid, block, 0, stream, S_in, static_cast<TOut*>(p.o), S_out,
-                     p.cu_seqlens, chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws, p.ckpt,
-                     ck_chunks, p.ckpt_slots, ckpt_off, c_lo, c_hi);
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, jobs, static_cast<TOut*>(p.o), p.cu_seqlens,
+                     chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws, p.ckpt, ck_chunks,
+                     p.ckpt_slots, ckpt_off);
   return hipGetLastError();
 }
 
@@ -959,9 +1036,44 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   const bool two = pairs * NSTRIP >= 4LL * n_cu;
   hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
   if (e != hipSuccess) return e;
-  return p.out_bf16
-             ? launch_rec<uint16_t>(p, stream, two, pairs, p.S0, p.S_T, 0, INT64_MAX, chunk_off, ckpt_off, ws)
-             : launch_rec<float>(p, stream, two, pairs, p.S0, p.S_T, 0, INT64_MAX, chunk_off, ckpt_off, ws);
+  auto rec = [&](const RecJobs& jobs, int n_jobs) {
+    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws)
+                      : launch_rec<float>(p, stream, two, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws);
+  };
+  RecJobs jobs = {};
+  const int P = n_segments(p);
+  if (P == 1) {  // one walk over every chunk
+    jobs.job[0] = RecJob{0, INT64_MAX, p.S0, p.S_T, REC_OUTPUT};
+    return rec(jobs, 1);
+  }
+  // Segmented walk (sequence split of the transition form): the chunks of each sequence are
+  // cut at b_1 < ... < b_{P-1}. Pass 1 walks segment 0 from S0 (its exit is segment 1's entry)
+  // and, at the same time, every middle segment p from zeros (Z_p) and from the identity with
+  // V = 0 (Phi_p). Then entry_{p+1} = Phi_p entry_p + Z_p, in order. Pass 2 walks segments
+  // 1 .. P-1 from their entries, all at once.
+  const int64_t span = ((p.T + C - 1) / C + P - 1) / P;  // chunks per segment (T bounds any sequence)
+  float* buf = reinterpret_cast<float*>(ws + segment_buffers_offset(p));
+  const size_t ns = state_bytes(p) / sizeof(float);
+  auto entry = [&](int q) { return buf + (size_t)(q - 1) * ns; };                   // q = 1 .. P-1
+  auto summ = [&](int q) { return buf + (size_t)(P - 1 + q - 1) * ns; };            // q = 1 .. P-2
+  auto trans = [&](int q) { return buf + (size_t)(P - 1 + P - 2 + q - 1) * ns; };   // q = 1 .. P-2
+  int n = 0;
+  jobs.job[n++] = RecJob{0, span, p.S0, entry(1), REC_OUTPUT};
+  for (int q = 1; q <= P - 2; ++q) {
+    jobs.job[n++] = RecJob{q * span, (q + 1) * span, nullptr, summ(q), REC_SUMMARY};
+    jobs.job[n++] = RecJob{q * span, (q + 1) * span, nullptr, trans(q), REC_TRANSITION};
+  }
+  if ((e = rec(jobs, n)) != hipSuccess) return e;
+  for (int q = 1; q <= P - 2; ++q) {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(pairs * NSTRIP)), dim3(256), 0, stream,
+                       trans(q), entry(q), summ(q), entry(q + 1), pairs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  n = 0;
+  for (int q = 1; q <= P - 1; ++q)
+    jobs.job[n++] = RecJob{q * span, q == P - 1 ? INT64_MAX : (q + 1) * span, entry(q),
+                           q == P - 1 ? p.S_T : nullptr, REC_OUTPUT};
+  return rec(jobs, n);
 }
 
 }  // namespace kda

@@ -31,6 +31,7 @@ struct ChunkPlan {
   int ckpt_every;   // tokens between checkpoints (a multiple of chunk), 0 = none
   int ckpt_slots;
   bool pairwise_diag;  // matrix-core path: diagonal tiles pairwise (no decay bound needed)
+  int segments;        // matrix-core path: walk each sequence in this many segments (>= 3), else 1
 };
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -112,6 +112,17 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *              sum_n floor(len_n / ckpt_every) slots gets every checkpoint; that sum is at
  *              most floor(B * T / ckpt_every)). ckpt must not overlap any input, o, S_T or
  *              the workspace.
+ *   segments   0, 1 or 2: every sequence is walked chunk after chunk (the default). 3 .. 8:
+ *              the matrix-core path cuts each sequence into that many segments and walks them
+ *              in parallel with the transition form of a segment, S_exit = Phi S_entry + Z
+ *              (orkas.ai Kimi K3 page, serving-infrastructure section on splitting a sequence):
+ *              one pass computes every middle segment's transition Phi and zero-start summary
+ *              Z alongside the first segment, the entries follow in order from those, and a
+ *              second pass walks the remaining segments from their entries. It trades about
+ *              twice the recurrence work for more parallelism, which pays when few (sequence,
+ *              head) pairs leave the GPU idle. The result equals the sequential walk to
+ *              rounding; the workspace grows by (3 segments - 5) state-sized buffers. Other
+ *              paths ignore it.
  */
 typedef struct {
     int B, T, H, dk, dv, chunk;
@@ -128,6 +139,7 @@ typedef struct {
     float* ckpt;
     int ckpt_every;
     int ckpt_slots;
+    int segments;
 } kda_chunk_args;
 
 #define KDA_FLAG_GENERIC 1u

@@ -33,7 +33,7 @@ def test_exports_every_declared_function(b):
                           "kda_abi_version"}
     for n in names:
         assert hasattr(b.lib(), n), n
-    assert b.lib().kda_abi_version() == b.ABI_VERSION == 2
+    assert b.lib().kda_abi_version() == b.ABI_VERSION == 3
 
 
 def test_status_strings(b):
@@ -67,7 +67,7 @@ def call_chunk(b, a):
 
 @pytest.mark.parametrize("field,value,status", [
     ("dk", 96, 2), ("dv", 256, 2), ("chunk", 48, 2), ("B", 0, 2), ("T", -1, 2), ("H", 0, 2),
-    ("act_dtype", 7, 3), ("gate_dtype", 0, 3), ("flags", 8, 4), ("flags", 4, 4),
+    ("act_dtype", 7, 3), ("gate_dtype", 0, 3), ("flags", 8, 4), ("flags", 4, 4), ("segments", 9, 2), ("segments", -1, 2),
 ])
 def test_chunk_rejects_bad_shapes_and_dtypes(b, field, value, status):
     rc, msg = call_chunk(b, base_args(b, **{field: value}))
