@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   //   operands: lent column operands k cf, fp32 [3][4][64][8]          [0, 24576)
   //             Ktil^T staging, fp16 [channel][row]                     [24576, 43008)
   //             Kbar^T staging (kept until W is formed)                 [43008, 61440)
-  //   inverse:  A fp32 [64][AS] [0, 17408), T [17408, 34816), scratch [34816, 37888)
+  //   inverse:  A fp32 [64][AS] [0, 17408), T [17408, 34816)
   //   products: V^T staging [0, 18432), once M is in registers
   //   last:     W^T [0, 18432), Utilde^T hi [18432, 36864), lo [36864, 55296)
   // pairwise tiles stage per wave G fp32 [16][132] and k, q bf16 [16][136] first
@@ -201,7 +201,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   _Float16* KBs = reinterpret_cast<_Float16*>(arena + 43008);
   float* A32 = reinterpret_cast<float*>(arena);
   float* T32 = reinterpret_cast<float*>(arena + 17408);
-  float* Xs = reinterpret_cast<float*>(arena + 34816);
   _Float16* VTs = reinterpret_cast<_Float16*>(arena);
   _Float16* WTs = reinterpret_cast<_Float16*>(arena);
   _Float16* UTh = reinterpret_cast<_Float16*>(arena + STG);
@@ -477,32 +476,31 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     for (int i = 0; i < 16; ++i) T32[(o + i) * AS + o + j] = col[i];
   }
   __syncthreads();
-  // ---- off-diagonal blocks, by distance from the diagonal:
-  //      T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb
-  {
-    const int i = t >> 4, jj = t & 15;
+  // ---- off-diagonal blocks, by distance L from the diagonal, on the fp32 matrix cores:
+  //      T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb; at distance L wave w < 4 - L takes block
+  //      (w + L, w). v_mfma_f32_16x16x4_f32 contracts four indices per step; step s uses
+  //      k = 4 (l >> 4) + s, so the accumulator X (lane: rows 4 (l >> 4) + i of column l & 15)
+  //      is directly the B operand of the product with T_aa.
 #pragma unroll
-    for (int L = 1; L < 4; ++L) {
-      for (int a = L; a < 4; ++a) {
-        const int bb = a - L;
-        float x = 0.f;
-        for (int cc = bb; cc < a; ++cc)
+  for (int L = 1; L < 4; ++L) {
+    if (w < 4 - L) {
+      const int a = w + L, bb = w;
+      floatx4 X = {0.f, 0.f, 0.f, 0.f};
+      for (int cc = bb; cc < a; ++cc) {
+        const floatx4 av = *reinterpret_cast<const floatx4*>(&A32[(16 * a + m) * AS + 16 * cc + 4 * gq]);
 #pragma unroll
-          for (int mm = 0; mm < 16; ++mm)
-            x += A32[(16 * a + i) * AS + 16 * cc + mm] * T32[(16 * cc + mm) * AS + 16 * bb + jj];
-        Xs[(a - L) * 256 + i * 16 + jj] = x;
+        for (int st = 0; st < 4; ++st)
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], T32[(16 * cc + 4 * gq + st) * AS + 16 * bb + m],
+                                                   X, 0, 0, 0);
       }
-      __syncthreads();
-      for (int a = L; a < 4; ++a) {
-        const int bb = a - L;
-        float x = 0.f;
+      const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[(16 * a + m) * AS + 16 * a + 4 * gq]);
+      floatx4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mm = 0; mm < 16; ++mm)
-          x += T32[(16 * a + i) * AS + 16 * a + mm] * Xs[(a - L) * 256 + mm * 16 + jj];
-        T32[(16 * a + i) * AS + 16 * bb + jj] = -x;
-      }
-      __syncthreads();
+      for (int st = 0; st < 4; ++st) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[st], X[st], Y, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T32[(16 * a + 4 * gq + i) * AS + 16 * bb + m] = -Y[i];
     }
+    __syncthreads();
   }
   // ---- M = T diag(beta): A-operand fragments of row tile w (blocks right of it are zero)
   half8 mfr[2];
