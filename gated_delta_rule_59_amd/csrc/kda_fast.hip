@@ -13,7 +13,10 @@
 // Two kernels.
 //  prep_kernel (one workgroup per chunk and head, all chunks in parallel): the per-channel
 //    cumulative log-decay; A and Aqk on the matrix cores; the inverse (I + A)^{-1} by
-//    blocked forward substitution in LDS; then W, Utilde, Qhat, Ohat on the matrix cores.
+//    blocked forward substitution in LDS; then, with P = Aqk M, W = M Kbar, Utilde = M V,
+//    Qhat = Qbar - P Kbar and Ohat = P V on the matrix cores. Channel-major (transposed)
+//    operands come from products with an identity fragment, so no LDS staging array is
+//    needed and three workgroups fit one CU.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
 //    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
 //    and result tiles (1 KiB = 64 lanes x 4 fp32).
@@ -176,35 +179,39 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 // generation (each e^{G_r - G_j} formed per pair and channel, in fp32 on the vector ALUs),
 // which needs no bound on the decay: the ablation that measures what the bound buys.
 template <bool PAIRWISE>
-__global__ __launch_bounds__(256, 2) void prep_kernel(
+__global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
     int n_seq, uint8_t* __restrict__ ws, int c_lo, int c_span) {
-  constexpr int TR = C + 8;         // row stride (fp16) of the channel-major staging arrays
-  constexpr int AS = C + 4;         // row stride (fp32) of A and T
-  constexpr int STG = DK * TR * 2;  // bytes of one staging array
-  // One LDS arena reused phase by phase (byte ranges):
-  //   operands: lent column operands k cf, fp32 [3][4][64][8]          [0, 24576)
-  //             Ktil^T staging, fp16 [channel][row]                     [24576, 43008)
-  //             Kbar^T staging (kept until W is formed)                 [43008, 61440)
-  //   inverse:  A fp32 [64][AS] [0, 17408), T [17408, 34816)
-  //   products: V^T staging [0, 18432), once M is in registers
-  //   last:     W^T [0, 18432), Utilde^T hi [18432, 36864), lo [36864, 55296)
-  // pairwise tiles stage per wave G fp32 [16][132] and k, q bf16 [16][136] first
+  constexpr int AS = C + 4;  // row stride (fp32) of A and T
+  // One LDS arena reused phase by phase (byte ranges), 51.5 KB so that three workgroups share
+  // a CU:
+  //   tile products: lent column operands k cf, fp32 [3][4][64][8]     [0, 24576)
+  //                  per-channel tables (tile totals and factors)     [24576, 32256)
+  //                  Kbar^T fragments (kept until the last products)  [34816, 51200)
+  //   inverse:       A fp32 [64][AS] [0, 17408), T [17408, 34816)
+  //   products:      V fragments [0, 16384), once M and P are in registers
+  // A fragment array holds 16 fragments [16-column tile][k-step over chunk rows], each in
+  // MFMA operand order (64 lanes x 8 fp16).
+  // The pairwise ablation first stages per wave G fp32 [16][132] and k, q bf16 [16][136].
   constexpr int PW_G = 16 * 132 * 4, PW_KQ = 16 * 136 * 2, PW_WAVE = PW_G + 2 * PW_KQ;
-  __shared__ __align__(16) unsigned char arena[PAIRWISE ? 4 * PW_WAVE : 61440];
-  __shared__ __align__(16) float TOT[4][DK], PCH[4][DK], ECH[4][DK], XCH[3][DK];
+  constexpr int OFF_TAB = PAIRWISE ? 4 * PW_WAVE : 24576;
+  constexpr int OFF_KBF = 34816;
+  constexpr int ARENA = PAIRWISE ? OFF_TAB + 7680 : 51200;
+  __shared__ __align__(16) unsigned char arena[ARENA];
   __shared__ __align__(16) float Bs[C];
   float* KC = reinterpret_cast<float*>(arena);
-  _Float16* KTs = reinterpret_cast<_Float16*>(arena + 24576);
-  _Float16* KBs = reinterpret_cast<_Float16*>(arena + 43008);
+  float(*TOT)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB);
+  float(*PCH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 2048);
+  float(*ECH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 4096);
+  float(*XCH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 6144);
+  half8* KBF = reinterpret_cast<half8*>(arena + OFF_KBF);
   float* A32 = reinterpret_cast<float*>(arena);
   float* T32 = reinterpret_cast<float*>(arena + 17408);
-  _Float16* VTs = reinterpret_cast<_Float16*>(arena);
-  _Float16* WTs = reinterpret_cast<_Float16*>(arena);
-  _Float16* UTh = reinterpret_cast<_Float16*>(arena + STG);
-  _Float16* UTl = reinterpret_cast<_Float16*>(arena + 2 * STG);
+  half8* VBF = reinterpret_cast<half8*>(arena);
+  static_assert(!PAIRWISE || OFF_TAB + 7680 <= ARENA, "layout");
+  static_assert(4 * PW_WAVE <= (PAIRWISE ? ARENA : 1 << 30), "layout");
 
   const int h = blockIdx.x % H;
   const int64_t cid = blockIdx.x / H;
@@ -239,9 +246,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   // ---- this lane's 32 elements of row 16w + m of k, q, g, v (rows past the end read as 0)
   u16x4 kraw[4][2], qraw[4][2], graw[4][2], vraw[4][2];
   uint16_t braw;
+  const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
   {
-    const int64_t tr = (tok0 + min(row, Cn - 1)) * H + h;
-    const int64_t erow = tr * DK;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -250,9 +256,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         graw[ks][hf] = *reinterpret_cast<const u16x4*>(g + e);
         kraw[ks][hf] = *reinterpret_cast<const u16x4*>(k + e);
         qraw[ks][hf] = *reinterpret_cast<const u16x4*>(q + e);
-        vraw[ks][hf] = *reinterpret_cast<const u16x4*>(v + e);
       }
-    braw = beta[tr];
+    braw = beta[(tok0 + min(row, Cn - 1)) * H + h];
   }
   // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
   float gs[4][8];
@@ -336,72 +341,95 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       if (4 * gq + i > m) pw_k[i] = pw_q[i] = 0.f;
     __syncthreads();  // the arena is reused below
   }
-  // ---- per-element factors and operands
-  float kr[4][8], qr[4][8], kd[4][8];  // k rf, q rf, k / rf
-  half8 qbar[4];                       // Qbar as A-operand fragments of row tile w
+  // identity fragments: as the B operand, idf[hf] copies channel tile hf of a 32-channel
+  // k-step, so (row fragment) x idf[hf] is the row tile's 16 x 16 block with each lane holding
+  // four rows of one channel, i.e. half of a channel-major (transposed) fragment. Exact: every
+  // product is a value times one or zero.
+  half8 idf[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      idf[hf][i] = static_cast<_Float16>((i >> 2) == hf && 4 * gq + (i & 3) == m ? 1.f : 0.f);
+  // half-fragment slot of this wave's 16 rows in a transposed fragment [tile ct][k-step w / 2]
+  auto half_slot = [&](int ct) { return ((ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8; };
+  auto store_half = [&](uint8_t* base, int ct, const floatx4& d) {
+    half4 hv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(d[i]);
+    *reinterpret_cast<half4*>(base + half_slot(ct)) = hv;
+  };
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- column operands: k cf lent to later row tiles, and Ktil^T fragments (workspace)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    floatx4 tw[2], pe[2], ee[2];
+    floatx4 kc[2];
+    half8 kt16;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int c0 = 32 * ks + 16 * hf + 4 * gq;
-      tw[hf] = *reinterpret_cast<const floatx4*>(&TOT[w][c0]);
-      pe[hf] = *reinterpret_cast<const floatx4*>(&PCH[w][c0]);
-      ee[hf] = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
-    }
-    floatx4 kc[2];
+      const floatx4 tw = *reinterpret_cast<const floatx4*>(&TOT[w][c0]);
+      const floatx4 ee = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int hf = i >> 2, j = i & 3;
-      const int ch = 32 * ks + 16 * hf + 4 * gq + j;
-      const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
-      const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
-      const float s = gs[ks][i];
-      const float rf = exp2f(s);
-      const float cf = exp2f(tw[hf][j] - s);
-      kr[ks][i] = kv * rf;
-      qr[ks][i] = qv * rf;
-      kd[ks][i] = kv * __builtin_amdgcn_rcpf(rf);
-      kc[hf][j] = kv * cf;
-      qbar[ks][i] = static_cast<_Float16>(qr[ks][i] * pe[hf][j]);
-      KBs[ch * TR + row] = static_cast<_Float16>(kr[ks][i] * pe[hf][j]);
-      KTs[ch * TR + row] = static_cast<_Float16>(kc[hf][j] * ee[hf][j]);
+      for (int j = 0; j < 4; ++j) {
+        const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
+        kc[hf][j] = kv * exp2f(tw[j] - gs[ks][4 * hf + j]);  // k e^{Gend_w - G_r}
+        kt16[4 * hf + j] = static_cast<_Float16>(kc[hf][j] * ee[j]);
+      }
     }
-    if (w < 3) {  // column operand k cf lent to later row tiles
+    if (w < 3) {
       float* kcp = KC + ((w * 4 + ks) * 64 + l) * 8;
       *reinterpret_cast<floatx4*>(kcp) = kc[0];
       *reinterpret_cast<floatx4*>(kcp + 4) = kc[1];
     }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) store_half(blk + OFF_KT, 2 * ks + hf, mfma_f16(kt16, idf[hf], zero));
   }
   __syncthreads();
-  // ---- Ktil^T fragments [dk tile][k-step over chunk rows]: four per wave
-#pragma unroll
-  for (int jf = 0; jf < 4; ++jf) {
-    const int f = w * 4 + jf;
-    const int mt = f >> 1, ks = f & 1;
-    *reinterpret_cast<half8*>(blk + OFF_KT + f * 1024 + l * 16) =
-        lds_frag(KTs + (16 * mt + m) * TR + 32 * ks, gq);
-  }
-  // ---- A and Aqk tiles of row tile w. Each tile is computed as (column operand) x (row
-  //      operand), i.e. transposed, so lane l ends with entries (16w + l&15, 16bb + 4 gq + i).
+  // ---- per k-step: row factors, Qbar, Kbar^T fragments (LDS), and the A and Aqk tiles of row
+  //      tile w. Each tile is computed as (column operand) x (row operand), i.e. transposed,
+  //      so lane l ends with entries (16w + l&15, 16bb + 4 gq + i).
   floatx4 akk[4], aqk[4];
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
-    akk[bb] = bb == w ? pw_k : floatx4{0.f, 0.f, 0.f, 0.f};
-    aqk[bb] = bb == w ? pw_q : floatx4{0.f, 0.f, 0.f, 0.f};
+    akk[bb] = bb == w ? pw_k : zero;
+    aqk[bb] = bb == w ? pw_q : zero;
   }
+  half8 qbar[4];  // Qbar as A-operand fragments of row tile w
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    float kr[8], qr[8], kd[8];
+    half8 kb16;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const floatx4 pe = *reinterpret_cast<const floatx4*>(&PCH[w][32 * ks + 16 * hf + 4 * gq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * hf + j;
+        const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
+        const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
+        const float rf = exp2f(gs[ks][i]);  // e^{G_r - ref_w}
+        kr[i] = kv * rf;
+        qr[i] = qv * rf;
+        kd[i] = kv * __builtin_amdgcn_rcpf(rf);
+        qbar[ks][i] = static_cast<_Float16>(qr[i] * pe[j]);
+        kb16[i] = static_cast<_Float16>(kr[i] * pe[j]);
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      store_half(reinterpret_cast<uint8_t*>(KBF), 2 * ks + hf, mfma_f16(kb16, idf[hf], zero));
     half8 rk16, rq16;
     bf16x8 rkh, rkl, rqh, rql, ch, cl;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      rk16[i] = static_cast<_Float16>(kr[ks][i]);
-      rq16[i] = static_cast<_Float16>(qr[ks][i]);
+      rk16[i] = static_cast<_Float16>(kr[i]);
+      rq16[i] = static_cast<_Float16>(qr[i]);
       __bf16 hh, ll;
-      split_bf16(kr[ks][i], hh, ll); rkh[i] = hh; rkl[i] = ll;
-      split_bf16(qr[ks][i], hh, ll); rqh[i] = hh; rql[i] = ll;
-      split_bf16(kd[ks][i], hh, ll); ch[i] = hh; cl[i] = ll;
+      split_bf16(kr[i], hh, ll); rkh[i] = hh; rkl[i] = ll;
+      split_bf16(qr[i], hh, ll); rqh[i] = hh; rql[i] = ll;
+      split_bf16(kd[i], hh, ll); ch[i] = hh; cl[i] = ll;
     }
     // diagonal tile: column factor up to e^80, split bf16
     if constexpr (!PAIRWISE) {
@@ -435,7 +463,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       aqk[bb] = mfma_f16(c16, rq16, aqk[bb]);
     }
   }
-  __syncthreads();  // the lent operands and Ktil^T staging are dead: A and T take the arena
+  // v is first needed after the inverse: its load latency overlaps the substitution
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      vraw[ks][hf] = *reinterpret_cast<const u16x4*>(v + erow + 32 * ks + 16 * hf + 4 * gq);
+  __syncthreads();  // the lent operands and the tables are dead: A and T take the arena
   // ---- beta-scaled A rows into LDS (entries on or above the diagonal are never read);
   //      Aqk (lower, diagonal included) as A-operand fragments hi + lo in registers
   {
@@ -485,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   for (int L = 1; L < 4; ++L) {
     if (w < 4 - L) {
       const int a = w + L, bb = w;
-      floatx4 X = {0.f, 0.f, 0.f, 0.f};
+      floatx4 X = zero;
       for (int cc = bb; cc < a; ++cc) {
         const floatx4 av = *reinterpret_cast<const floatx4*>(&A32[(16 * a + m) * AS + 16 * cc + 4 * gq]);
 #pragma unroll
@@ -494,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                                                    X, 0, 0, 0);
       }
       const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[(16 * a + m) * AS + 16 * a + 4 * gq]);
-      floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+      floatx4 Y = zero;
 #pragma unroll
       for (int st = 0; st < 4; ++st) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[st], X[st], Y, 0, 0, 0);
 #pragma unroll
@@ -502,8 +536,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     }
     __syncthreads();
   }
-  // ---- M = T diag(beta): A-operand fragments of row tile w (blocks right of it are zero)
-  half8 mfr[2];
+  // ---- M = T diag(beta) as A-operand fragments of row tile w, and P = Aqk M as P^T = M^T Aqk^T
+  //      (own rows again), split fp16 hi + lo. M is lower triangular: entries of tile blocks
+  //      right of the diagonal (never written) are taken as zero.
+  half8 mfr[2], pfh[2], pfl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -515,84 +551,82 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       for (int ii = 0; ii < 4; ++ii)
         mfr[ks][4 * hf + ii] = static_cast<_Float16>(bb <= w ? tv[ii] * bv[ii] : 0.f);
     }
-  __syncthreads();  // T is in registers: V^T takes the front of the arena
+  {
+    floatx4 pt[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ch = 32 * ks + 16 * (i >> 2) + 4 * gq + (i & 3);
-      VTs[ch * TR + row] =
-          static_cast<_Float16>(row_ok ? bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]) : 0.f);
-    }
-  __syncthreads();
-  // ---- W = M Kbar (as W^T = Kbar^T M^T, which leaves each lane with its own row) and
-  //      Utilde = M V, row tile w, every 16-column tile
-  half4 wq[8];              // W rounded to fp16: row 16w + m, channels 16ct + 4gq + i
-  half4 uth[8], utl[8];     // Utilde hi + lo: rows 16w + 4gq + i, column 16ct + m
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    floatx4 aw = {0.f, 0.f, 0.f, 0.f}, au = aw;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      aw = mfma_f16(lds_frag(KBs + (16 * ct + m) * TR + 32 * ks, gq), mfr[ks], aw);
-      au = mfma_f16(mfr[ks], lds_frag(VTs + (16 * ct + m) * TR + 32 * ks, gq), au);
-    }
-    *reinterpret_cast<floatx4*>(blk + OFF_UT + (ct * 4 + w) * 1024 + l * 16) = au;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wq[ct][i] = static_cast<_Float16>(aw[i]);
-      _Float16 hh, ll;
-      split_f16(au[i], hh, ll);
-      uth[ct][i] = hh;
-      utl[ct][i] = ll;
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    *reinterpret_cast<half8*>(blk + OFF_WN + (kk * 4 + w) * 1024 + l * 16) =
-        -frag_from_halves(wq[2 * kk], wq[2 * kk + 1]);
-  __syncthreads();  // Kbar^T and V^T are dead: W^T and Utilde^T take the arena
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) WTs[(16 * ct + 4 * gq + i) * TR + row] = wq[ct][i];
-    *reinterpret_cast<half4*>(&UTh[(16 * ct + m) * TR + 16 * w + 4 * gq]) = uth[ct];
-    *reinterpret_cast<half4*>(&UTl[(16 * ct + m) * TR + 16 * w + 4 * gq]) = utl[ct];
-  }
-  __syncthreads();
-  // ---- Qhat = Qbar - Aqk W (via (Aqk W)^T = W^T Aqk^T, own rows again) and Ohat = Aqk Utilde
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    floatx4 aw[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int ct = 2 * kk + hf;
-      aw[hf] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 4; ++ct) {
+      pt[ct] = zero;
+      if (ct > w) continue;  // P is lower triangular
+      const float bj = Bs[16 * ct + m];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const half8 wf = lds_frag(WTs + (16 * ct + m) * TR + 32 * ks, gq);
-        aw[hf] = mfma_f16(wf, ahi[ks], aw[hf]);
-        aw[hf] = mfma_f16(wf, alo[ks], aw[hf]);
+        half8 mt;  // M^T fragment: row 16ct + m of M^T = column of M, rows 32ks + kslot(gq, i)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int x = 32 * ks + kslot(gq, i);
+          mt[i] = static_cast<_Float16>((x >> 4) >= ct ? T32[x * AS + 16 * ct + m] * bj : 0.f);
+        }
+        pt[ct] = mfma_f16(mt, ahi[ks], pt[ct]);
+        pt[ct] = mfma_f16(mt, alo[ks], pt[ct]);
       }
     }
-    half8 qh;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        _Float16 hh, ll;
+        split_f16(pt[2 * ks + (i >> 2)][i & 3], hh, ll);
+        pfh[ks][i] = hh;
+        pfl[ks][i] = ll;
+      }
+  }
+  __syncthreads();  // T is dead: V fragments take the front of the arena
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    half8 v16;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - aw[i >> 2][i & 3]);
-    *reinterpret_cast<half8*>(blk + OFF_QH + (kk * 4 + w) * 1024 + l * 16) = qh;
+      v16[i] = static_cast<_Float16>(row_ok ? bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]) : 0.f);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      store_half(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
   }
+  __syncthreads();
+  // ---- per 16-column tile ct: W^T = Kbar^T M^T and (P Kbar)^T = Kbar^T P^T (own rows, so
+  //      that -W and Qhat = Qbar - P Kbar are A-operand fragments), Utilde = M V and
+  //      Ohat = P V (result tiles in the walk's accumulator layout)
+  floatx4 wt_prev = zero, pk_prev = zero;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    floatx4 ao = {0.f, 0.f, 0.f, 0.f};
+    floatx4 aw = zero, ap = zero, au = zero, ao = zero;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const half8 uh = lds_frag(UTh + (16 * ct + m) * TR + 32 * ks, gq);
-      const half8 ul = lds_frag(UTl + (16 * ct + m) * TR + 32 * ks, gq);
-      ao = mfma_f16(ahi[ks], uh, ao);
-      ao = mfma_f16(ahi[ks], ul, ao);
-      ao = mfma_f16(alo[ks], uh, ao);
+    for (int kk = 0; kk < 2; ++kk) {
+      const half8 kb = KBF[(ct * 2 + kk) * 64 + l];
+      const half8 vb = VBF[(ct * 2 + kk) * 64 + l];
+      aw = mfma_f16(kb, mfr[kk], aw);
+      ap = mfma_f16(kb, pfh[kk], ap);
+      ap = mfma_f16(kb, pfl[kk], ap);
+      au = mfma_f16(mfr[kk], vb, au);
+      ao = mfma_f16(pfh[kk], vb, ao);
+      ao = mfma_f16(pfl[kk], vb, ao);
     }
+    *reinterpret_cast<floatx4*>(blk + OFF_UT + (ct * 4 + w) * 1024 + l * 16) = au;
     *reinterpret_cast<floatx4*>(blk + OFF_OH + (ct * 4 + w) * 1024 + l * 16) = ao;
+    if (ct & 1) {  // tiles 2kk and 2kk + 1 form the fragments of k-step kk over dk
+      const int kk = ct >> 1;
+      half8 wn, qh;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wv = i < 4 ? wt_prev[i] : aw[i - 4];
+        const float pv = i < 4 ? pk_prev[i] : ap[i - 4];
+        wn[i] = -static_cast<_Float16>(wv);
+        qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - pv);
+      }
+      *reinterpret_cast<half8*>(blk + OFF_WN + (kk * 4 + w) * 1024 + l * 16) = wn;
+      *reinterpret_cast<half8*>(blk + OFF_QH + (kk * 4 + w) * 1024 + l * 16) = qh;
+    }
+    wt_prev = aw;
+    pk_prev = ap;
   }
 }
 
