@@ -129,11 +129,49 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 // ---------------------------------------------------------------- prep
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zero and stores
+// past the end are dropped, which is how partial chunks are masked without branches.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// 8-byte workspace stores go through a buffer resource of the block: the lane's byte offset
+// is one VGPR and the constant part an SGPR, so no 64-bit address per store stays live.
+// 16-byte stores are global stores: a buffer store wider than 8 bytes with an SGPR offset
+// gets no wait state before its data registers are rewritten, and on gfx950 the last dword of
+// some lanes was then read after the rewrite (wrong workspace values, intermittently).
+__device__ __forceinline__ void st_half(rsrc_t r, int lane_off, int off, const half4& f) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f), r, lane_off, off, 0);
+}
 
 // x from lane m - S of the same 16-lane DPP row (0 for m < S).
 template <int S>
 __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + S, 0xF, 0xF, true));
+}
+// 2^x for x in [-116, 0], the range of a decay factor across one 16-token tile (each step's
+// log-decay is >= -5): the hardware exp2 is exact to its ulp bound there and needs none of
+// the scaling that exp2f adds for arguments below -126.
+__device__ __forceinline__ float exp2_tile(float x) { return __builtin_amdgcn_exp2f(x); }
+// Eight fp32 values split into bf16 hi (nearest) + lo (the nearest bf16 to the residual), two
+// values per conversion; hi is widened back by shifting its halves into place.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u32x4 h, r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * i], x[2 * i + 1]}, bf16x2));
+    const float h0 = __uint_as_float(hu << 16), h1 = __uint_as_float(hu & 0xffff0000u);
+    h[i] = hu;
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * i] - h0, x[2 * i + 1] - h1}, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, r);
 }
 // Inclusive prefix sum over the 16 lanes of a DPP row.
 __device__ __forceinline__ float row_scan(float x) {
@@ -236,6 +274,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   const int64_t tok0 = si.tok0 + c_in * C;
   const int Cn = (int)min((int64_t)C, si.len - c_in * C);
   uint8_t* blk = ws + ((size_t)(si.cid0 + c_in) * H + h) * kBlockBytes;
+  const rsrc_t wsr = make_rsrc(blk, (int64_t)kBlockBytes);
 
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -293,7 +332,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     if (hf == 0) {
       XCH[0][c] = exp2f(t1);       // column factor of block (2, 0): e^{ref_2 - Gend_0}
       XCH[1][c] = exp2f(t1 + t2);  // (3, 0)
-      reinterpret_cast<float*>(blk + OFF_GAM)[c] = exp2f(gc);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(exp2f(gc)), wsr, c * 4, OFF_GAM, 0);
     } else {
       XCH[2][c] = exp2f(t2);       // (3, 1)
     }
@@ -351,13 +390,17 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       idf[hf][i] = static_cast<_Float16>((i >> 2) == hf && 4 * gq + (i & 3) == m ? 1.f : 0.f);
-  // half-fragment slot of this wave's 16 rows in a transposed fragment [tile ct][k-step w / 2]
-  auto half_slot = [&](int ct) { return ((ct * 2 + (w >> 1)) * 64 + l) * 16 + (w & 1) * 8; };
-  auto store_half = [&](uint8_t* base, int ct, const floatx4& d) {
+  // half-fragment slot of this wave's 16 rows in a transposed fragment [tile ct][k-step w / 2]:
+  // byte ct * 2048 + half_lane
+  const int half_lane = ((w >> 1) * 64 + l) * 16 + (w & 1) * 8;
+  auto to_half4 = [](const floatx4& d) {
     half4 hv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(d[i]);
-    *reinterpret_cast<half4*>(base + half_slot(ct)) = hv;
+    return hv;
+  };
+  auto store_half_lds = [&](uint8_t* base, int ct, const floatx4& d) {
+    *reinterpret_cast<half4*>(base + ct * 2048 + half_lane) = to_half4(d);
   };
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -374,7 +417,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
-        kc[hf][j] = kv * exp2f(tw[j] - gs[ks][4 * hf + j]);  // k e^{Gend_w - G_r}
+        kc[hf][j] = kv * exp2_tile(tw[j] - gs[ks][4 * hf + j]);  // k e^{Gend_w - G_r}
         kt16[4 * hf + j] = static_cast<_Float16>(kc[hf][j] * ee[j]);
       }
     }
@@ -384,18 +427,19 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
       *reinterpret_cast<floatx4*>(kcp + 4) = kc[1];
     }
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) store_half(blk + OFF_KT, 2 * ks + hf, mfma_f16(kt16, idf[hf], zero));
+    for (int hf = 0; hf < 2; ++hf)
+      st_half(wsr, half_lane, OFF_KT + (2 * ks + hf) * 2048, to_half4(mfma_f16(kt16, idf[hf], zero)));
   }
   __syncthreads();
   // ---- per k-step: row factors, Qbar, Kbar^T fragments (LDS), and the A and Aqk tiles of row
   //      tile w. Each tile is computed as (column operand) x (row operand), i.e. transposed,
   //      so lane l ends with entries (16w + l&15, 16bb + 4 gq + i).
-  floatx4 akk[4], aqk[4];
+  floatx4 akk[3], aqk[3];
+  // the diagonal tile has accumulators of its own, so that no register array is indexed by the
+  // (run-time) wave number
+  floatx4 akd = pw_k, aqd = pw_q;
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-    akk[bb] = bb == w ? pw_k : zero;
-    aqk[bb] = bb == w ? pw_q : zero;
-  }
+  for (int bb = 0; bb < 3; ++bb) akk[bb] = aqk[bb] = zero;
   half8 qbar[4];  // Qbar as A-operand fragments of row tile w
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -409,7 +453,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
         const int i = 4 * hf + j;
         const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
         const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
-        const float rf = exp2f(gs[ks][i]);  // e^{G_r - ref_w}
+        const float rf = exp2_tile(gs[ks][i]);  // e^{G_r - ref_w}
         kr[i] = kv * rf;
         qr[i] = qv * rf;
         kd[i] = kv * __builtin_amdgcn_rcpf(rf);
@@ -419,26 +463,25 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      store_half(reinterpret_cast<uint8_t*>(KBF), 2 * ks + hf, mfma_f16(kb16, idf[hf], zero));
+      store_half_lds(reinterpret_cast<uint8_t*>(KBF), 2 * ks + hf, mfma_f16(kb16, idf[hf], zero));
     half8 rk16, rq16;
-    bf16x8 rkh, rkl, rqh, rql, ch, cl;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       rk16[i] = static_cast<_Float16>(kr[i]);
       rq16[i] = static_cast<_Float16>(qr[i]);
-      __bf16 hh, ll;
-      split_bf16(kr[i], hh, ll); rkh[i] = hh; rkl[i] = ll;
-      split_bf16(qr[i], hh, ll); rqh[i] = hh; rql[i] = ll;
-      split_bf16(kd[i], hh, ll); ch[i] = hh; cl[i] = ll;
     }
+    bf16x8 rkh, rkl, rqh, rql, ch, cl;
+    split_bf16x8(kr, rkh, rkl);
+    split_bf16x8(qr, rqh, rql);
+    split_bf16x8(kd, ch, cl);
     // diagonal tile: column factor up to e^80, split bf16
     if constexpr (!PAIRWISE) {
-      akk[w] = mfma_bf16(ch, rkh, akk[w]);
-      akk[w] = mfma_bf16(ch, rkl, akk[w]);
-      akk[w] = mfma_bf16(cl, rkh, akk[w]);
-      aqk[w] = mfma_bf16(ch, rqh, aqk[w]);
-      aqk[w] = mfma_bf16(ch, rql, aqk[w]);
-      aqk[w] = mfma_bf16(cl, rqh, aqk[w]);
+      akd = mfma_bf16(ch, rkh, akd);
+      akd = mfma_bf16(ch, rkl, akd);
+      akd = mfma_bf16(cl, rkh, akd);
+      aqd = mfma_bf16(ch, rqh, aqd);
+      aqd = mfma_bf16(ch, rql, aqd);
+      aqd = mfma_bf16(cl, rqh, aqd);
     }
     // earlier tiles: factors <= 1, fp16
 #pragma unroll
@@ -475,8 +518,9 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   {
     const float br = Bs[row];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      if (bb <= w) *reinterpret_cast<floatx4*>(&A32[row * AS + 16 * bb + 4 * gq]) = br * akk[bb];
+    for (int bb = 0; bb < 3; ++bb)
+      if (bb < w) *reinterpret_cast<floatx4*>(&A32[row * AS + 16 * bb + 4 * gq]) = br * akk[bb];
+    *reinterpret_cast<floatx4*>(&A32[row * AS + 16 * w + 4 * gq]) = br * akd;
   }
   half8 ahi[2], alo[2];
 #pragma unroll
@@ -484,7 +528,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int bb = 2 * ks + (i >> 2), ii = i & 3;
-      const float a = (bb < w || (bb == w && 4 * gq + ii <= m)) ? aqk[bb][ii] : 0.f;
+      const float a = bb < w ? aqk[bb < 3 ? bb : 2][ii] : (bb == w && 4 * gq + ii <= m) ? aqd[ii] : 0.f;
       _Float16 hh, ll;
       split_f16(a, hh, ll);
       ahi[ks][i] = hh;
@@ -589,7 +633,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
       v16[i] = static_cast<_Float16>(row_ok ? bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]) : 0.f);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      store_half(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
+      store_half_lds(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
   }
   __syncthreads();
   // ---- per 16-column tile ct: W^T = Kbar^T M^T and (P Kbar)^T = Kbar^T P^T (own rows, so
@@ -631,14 +675,6 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
 }
 
 // ---------------------------------------------------------------- rec
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer resource over [base, base + bytes): loads past the end return zero and stores
-// past the end are dropped, which is how partial chunks are masked without branches.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
 __device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
