@@ -4,19 +4,20 @@
 // for a 64-token chunk entered with state S, G_r = sum_{j<=r} g_j per key channel:
 //   U' = M (V - Kbar S) = Utilde - W S,   M = (I + A)^{-1} diag(b),  W = M Kbar,  Utilde = M V
 //   A[r][j] = b_r sum_c k_r k_j e^{G_r - G_j} (j < r),   Aqk[r][j] = sum_c q_r k_j e^{G_r - G_j} (j <= r)
-//   O  = Qbar S + Aqk U' = Qhat S + Ohat,   Qhat = Qbar - Aqk W,   Ohat = Aqk Utilde
-//   S <- Diag(e^{G_C}) S + Ktil^T U',      Kbar = K e^{G}, Qbar = Q e^{G}, Ktil = K e^{G_C - G}.
-// Everything that does not depend on the entry state (W, Utilde, Qhat, Ohat, Ktil) is formed
-// for all chunks in parallel; the serial walk over the chunks then needs two products with
-// the state per chunk (W S for U', Qhat S for the outputs) and the state update.
+//   O  = Qbar S + Aqk U' = Qhat S + Ohat,   Qhat = Qbar - P Kbar,   Ohat = P V,   P = Aqk M
+//   S <- Diag(e^{G_C}) S + Ktil^T U' = Diag(e^{G_C}) S + Z - Phi S,   Phi = Ktil^T W,  Z = Ktil^T Utilde
+// with Kbar = K e^{G}, Qbar = Q e^{G}, Ktil = K e^{G_C - G}. Everything that does not depend on
+// the entry state (Phi, Z, Qhat, Ohat) is formed for all chunks in parallel; the serial walk
+// over the chunks then needs two products with the state per chunk (Phi S for the update,
+// Qhat S for the outputs), both of the state as it enters the chunk, so one exchange of the
+// state between waves per chunk suffices.
 //
 // Two kernels.
 //  prep_kernel (one workgroup per chunk and head, all chunks in parallel): the per-channel
 //    cumulative log-decay; A and Aqk on the matrix cores; the inverse (I + A)^{-1} by
-//    blocked forward substitution in LDS; then, with P = Aqk M, W = M Kbar, Utilde = M V,
-//    Qhat = Qbar - P Kbar and Ohat = P V on the matrix cores. Channel-major (transposed)
-//    operands come from products with an identity fragment, so no LDS staging array is
-//    needed and three workgroups fit one CU.
+//    blocked forward substitution in LDS; then P, Qhat, Ohat, W, Utilde, Phi and Z on the
+//    matrix cores. Channel-major (transposed) operands come from products with an identity
+//    fragment, so no LDS staging array is needed and three workgroups fit one CU.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
 //    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
 //    and result tiles (1 KiB = 64 lanes x 4 fp32).
@@ -31,10 +32,10 @@
 //  rec_kernel (one workgroup per sequence, head and 16 value columns, serial over chunks):
 //    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence.
 //    Eight waves in two roles. Waves 0-3 own 32 key rows of the state each and carry the
-//    dependency chain: U' = Utilde - W S for their 16 chunk rows, then the state update.
-//    Waves 4-7 compute the outputs Qhat S + Ohat of their 16 chunk rows from the same
-//    gathered state, off the chain. Columns of S evolve independently (the transition acts on
-//    the key side only), so splitting the value columns over workgroups is exact.
+//    dependency chain: S <- Diag(e^{G_C}) S + Z - Phi S for their rows. Waves 4-7 compute the
+//    outputs Qhat S + Ohat of their 16 chunk rows from the same gathered state, off the chain.
+//    Columns of S evolve independently (the transition acts on the key side only), so
+//    splitting the value columns over workgroups is exact.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -49,13 +50,16 @@ constexpr int NSTRIP = DV / 16;  // 16-column strips per (sequence, head)
 
 // Workspace block of one (chunk, head), byte offsets. Fragment f of a group starts at
 // group + f * 1024 (lane l's eight fp16 at + l * 16); result tile f likewise (four fp32).
-constexpr int OFF_WN = 0;        // -W as A operand: [k-step over dk (4)][row tile (4)]
-constexpr int OFF_QH = 16384;    // Qhat, same order
-constexpr int OFF_KT = 32768;    // Ktil^T: [dk tile (8)][k-step over chunk rows (2)]
-constexpr int OFF_UT = 49152;    // Utilde result tiles: [value tile (8)][row tile (4)]
-constexpr int OFF_OH = 81920;    // Ohat, same order
+constexpr int OFF_PHI = 0;       // Phi = Ktil^T W as A operand: [key row tile (8)][k-step over keys (4)]
+constexpr int OFF_QH = 32768;    // Qhat as A operand: [k-step over dk (4)][row tile (4)]
+constexpr int OFF_Z = 49152;     // Z = Ktil^T Utilde, fp16 tiles in accumulator layout:
+                                 //   [value tile (8)][key row pair (4)][lane][tile of the pair][4]
+constexpr int OFF_OH = 81920;    // Ohat result tiles, fp32: [value tile (8)][row tile (4)]
 constexpr int OFF_GAM = 114688;  // e^{G_C}, fp32 [128]
 constexpr size_t kBlockBytes = 115200;
+// Ktil^T fragments [dk tile (8)][k-step over chunk rows (2)] are parked in the Z region while
+// a workgroup of the prep kernel builds its block (Z is written after they are read).
+constexpr int OFF_KTMP = OFF_Z;
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -428,7 +432,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      st_half(wsr, half_lane, OFF_KT + (2 * ks + hf) * 2048, to_half4(mfma_f16(kt16, idf[hf], zero)));
+      st_half(wsr, half_lane, OFF_KTMP + (2 * ks + hf) * 2048, to_half4(mfma_f16(kt16, idf[hf], zero)));
   }
   __syncthreads();
   // ---- per k-step: row factors, Qbar, Kbar^T fragments (LDS), and the A and Aqk tiles of row
@@ -580,21 +584,10 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     }
     __syncthreads();
   }
-  // ---- M = T diag(beta) as A-operand fragments of row tile w, and P = Aqk M as P^T = M^T Aqk^T
-  //      (own rows again), split fp16 hi + lo. M is lower triangular: entries of tile blocks
-  //      right of the diagonal (never written) are taken as zero.
-  half8 mfr[2], pfh[2], pfl[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int bb = 2 * ks + hf;
-      const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[row * AS + 16 * bb + 4 * gq]);
-      const floatx4 bv = *reinterpret_cast<const floatx4*>(&Bs[16 * bb + 4 * gq]);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        mfr[ks][4 * hf + ii] = static_cast<_Float16>(bb <= w ? tv[ii] * bv[ii] : 0.f);
-    }
+  // ---- P = Aqk M as P^T = M^T Aqk^T (so that each lane ends with its own row of P), split
+  //      fp16 hi + lo. M = T diag(beta) is lower triangular: entries of tile blocks right of the
+  //      diagonal (never written) are taken as zero.
+  half8 pfh[2], pfl[2];
   {
     floatx4 pt[4];
 #pragma unroll
@@ -624,7 +617,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
         pfl[ks][i] = ll;
       }
   }
-  __syncthreads();  // T is dead: V fragments take the front of the arena
+  // ---- V fragments into the front of the arena (A is dead, T stays)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     half8 v16;
@@ -636,42 +629,120 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
       store_half_lds(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
   }
   __syncthreads();
-  // ---- per 16-column tile ct: W^T = Kbar^T M^T and (P Kbar)^T = Kbar^T P^T (own rows, so
-  //      that -W and Qhat = Qbar - P Kbar are A-operand fragments), Utilde = M V and
-  //      Ohat = P V (result tiles in the walk's accumulator layout)
-  floatx4 wt_prev = zero, pk_prev = zero;
+  // ---- row tile w: (P Kbar)^T = Kbar^T P^T, so that Qhat = Qbar - P Kbar comes out as
+  //      A-operand fragments, and Ohat = P V as result tiles in the walk's accumulator layout
+  floatx4 pk_prev = zero;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    floatx4 aw = zero, ap = zero, au = zero, ao = zero;
+    floatx4 ap = zero, ao = zero;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const half8 kb = KBF[(ct * 2 + kk) * 64 + l];
       const half8 vb = VBF[(ct * 2 + kk) * 64 + l];
-      aw = mfma_f16(kb, mfr[kk], aw);
       ap = mfma_f16(kb, pfh[kk], ap);
       ap = mfma_f16(kb, pfl[kk], ap);
-      au = mfma_f16(mfr[kk], vb, au);
       ao = mfma_f16(pfh[kk], vb, ao);
       ao = mfma_f16(pfl[kk], vb, ao);
     }
-    *reinterpret_cast<floatx4*>(blk + OFF_UT + (ct * 4 + w) * 1024 + l * 16) = au;
     *reinterpret_cast<floatx4*>(blk + OFF_OH + (ct * 4 + w) * 1024 + l * 16) = ao;
     if (ct & 1) {  // tiles 2kk and 2kk + 1 form the fragments of k-step kk over dk
       const int kk = ct >> 1;
-      half8 wn, qh;
+      half8 qh;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float wv = i < 4 ? wt_prev[i] : aw[i - 4];
-        const float pv = i < 4 ? pk_prev[i] : ap[i - 4];
-        wn[i] = -static_cast<_Float16>(wv);
-        qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - pv);
-      }
-      *reinterpret_cast<half8*>(blk + OFF_WN + (kk * 4 + w) * 1024 + l * 16) = wn;
+      for (int i = 0; i < 8; ++i)
+        qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - (i < 4 ? pk_prev[i] : ap[i - 4]));
       *reinterpret_cast<half8*>(blk + OFF_QH + (kk * 4 + w) * 1024 + l * 16) = qh;
     }
-    wt_prev = aw;
     pk_prev = ap;
   }
+  // ---- W = M Kbar and Utilde = M V for the column tiles 2w and 2w + 1, every chunk row, as
+  //      B-operand fragments [tile][k-step over chunk rows]: the result tile of row tile rt holds
+  //      rows 16 rt + 4 gq + i of column m, i.e. half of the fragment of k-step rt / 2. M's row
+  //      tiles come from T in LDS; Utilde is split fp16 hi + lo.
+  half8 wb[2][2], uh[2][2], ul[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    half8 mr[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int bb = 2 * kk + hf;
+        const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[(16 * rt + m) * AS + 16 * bb + 4 * gq]);
+        const floatx4 bv = *reinterpret_cast<const floatx4*>(&Bs[16 * bb + 4 * gq]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          mr[kk][4 * hf + ii] = static_cast<_Float16>(bb <= rt ? tv[ii] * bv[ii] : 0.f);
+      }
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc) {
+      const int ct = 2 * w + tc;
+      floatx4 dw = zero, du = zero;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dw = mfma_f16(mr[kk], KBF[(ct * 2 + kk) * 64 + l], dw);
+        du = mfma_f16(mr[kk], VBF[(ct * 2 + kk) * 64 + l], du);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 4 * (rt & 1) + i;
+        wb[tc][rt >> 1][slot] = static_cast<_Float16>(dw[i]);
+        _Float16 hh, ll;
+        split_f16(du[i], hh, ll);
+        uh[tc][rt >> 1][slot] = hh;
+        ul[tc][rt >> 1][slot] = ll;
+      }
+    }
+  }
+  __syncthreads();  // T is dead: Ktil^T fragments are copied from the workspace into its place
+  half8* KTL = reinterpret_cast<half8*>(arena + 17408);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int f = t + 256 * e;  // 16-byte unit of the 16 KiB fragment array
+    KTL[f] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(wsr, f * 16, OFF_KTMP, 0));
+  }
+  __syncthreads();
+  // ---- Phi = Ktil^T W for key rows kt and key columns 32w .. 32w + 31, computed as
+  //      Phi^T = W^T Ktil so that each lane ends with its own row: A-operand fragments (kt, w)
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    floatx4 d0 = zero, d1 = zero;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const half8 ktf = KTL[(kt * 2 + kk) * 64 + l];
+      d0 = mfma_f16(wb[0][kk], ktf, d0);
+      d1 = mfma_f16(wb[1][kk], ktf, d1);
+    }
+    half8 ph;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = static_cast<_Float16>(d0[i]);
+      ph[i + 4] = static_cast<_Float16>(d1[i]);
+    }
+    *reinterpret_cast<half8*>(blk + OFF_PHI + (kt * 4 + w) * 1024 + l * 16) = ph;
+  }
+  // ---- Z = Ktil^T Utilde for value tiles 2w and 2w + 1, every key row tile: the lane holds
+  //      key rows 16 kt + 4 gq + i of value column m, the walk's accumulator layout (fp16)
+#pragma unroll
+  for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      half8 zf;  // key row tiles 2kp and 2kp + 1: one 16-byte store
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kt = 2 * kp + u;
+        const half8 kf0 = KTL[(kt * 2) * 64 + l], kf1 = KTL[(kt * 2 + 1) * 64 + l];
+        floatx4 dz = zero, dz2 = zero;
+        dz = mfma_f16(kf0, uh[tt][0], dz);
+        dz2 = mfma_f16(kf0, ul[tt][0], dz2);
+        dz = mfma_f16(kf1, uh[tt][1], dz);
+        dz2 = mfma_f16(kf1, ul[tt][1], dz2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zf[4 * u + i] = static_cast<_Float16>(dz[i] + dz2[i]);
+      }
+      const int vt = 2 * w + tt;
+      *reinterpret_cast<half8*>(blk + OFF_Z + ((vt * 4 + kp) * 64 + l) * 16) = zf;
+    }
 }
 
 // ---------------------------------------------------------------- rec
@@ -710,17 +781,16 @@ __global__ __launch_bounds__(512) void rec_kernel(
     const uint8_t* __restrict__ ws, float* __restrict__ ckpt, int ckpt_chunks, int ckpt_slots,
     const int32_t* __restrict__ ckpt_off) {
   // blockIdx.x = job * blocks_per_job + (block within the job)
-  // A workgroup owns NT strips of 16 value columns. Two fp16 exchanges per chunk through
-  // LDS, each followed by a barrier: the state strips (all 128 key rows), which every wave
-  // needs whole for W S or Qhat S of its 16 chunk rows, and U' (all 64 chunk rows) for the
-  // state update. Both are stored column-major ([column][row]) so the rows a lane needs for
-  // a B operand are contiguous, with rows padded by 8 halves against bank conflicts. One
-  // buffer of each suffices: every read of a buffer happens between the barrier after its
-  // write and the next barrier, which precedes its next write.
+  // A workgroup owns NT strips of 16 value columns. One fp16 exchange per chunk through LDS,
+  // followed by one barrier: the state strips entering the chunk (all 128 key rows), which the
+  // state waves need whole for Phi S and the output waves for Qhat S. They are stored
+  // column-major ([column][row]) so the rows a lane needs for a B operand are contiguous, with
+  // rows padded by 8 halves against bank conflicts, in two buffers used by alternate chunks:
+  // the buffer of chunk c is read between barrier c and barrier c + 1, and written again only
+  // for chunk c + 2, after barrier c + 1.
   constexpr int NG = NSTRIP / NT;  // strip groups per (sequence, head)
-  constexpr int SR = DK + 8, UR = C + 8;
-  __shared__ __align__(16) _Float16 sx[NT * 16][SR];
-  __shared__ __align__(16) _Float16 ux[2][NT * 16][UR];
+  constexpr int SR = DK + 8;
+  __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];
 
   const RecJob job = jobs.job[blockIdx.x / jobs.blocks_per_job];
   const int64_t c_lo = job.c_lo, c_hi = job.c_hi;
@@ -747,8 +817,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
   const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * kBlockBytes;
   const size_t blk_step = (size_t)H * kBlockBytes;
 
-  // B operand of state strip nt for key rows 32 j + kslot(gq, i), column nn
-  auto state_frag = [&](int nt, int j) { return lds_frag(&sx[16 * nt + nn][32 * j], gq); };
+  // B operand of state strip nt for key rows 32 j + kslot(gq, i), column nn, from buffer bf
+  auto state_frag = [&](int bf, int nt, int j) { return lds_frag(&sx[bf][16 * nt + nn][32 * j], gq); };
   // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
   const int64_t ck_base =
       ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
@@ -780,24 +850,18 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // loop is unrolled by two, so no set is ever copied): a chunk's loads have two chunks'
     // time to arrive, which covers a first read of the workspace from HBM.
     struct Ops {
-      half8 wn[4], kt[2][2];
-      floatx4 ut[NT], gam[2];
+      half8 phi[2][4];  // Phi rows of key row tiles 2w + u, k-steps over keys
+      half8 z[NT];      // Z of both key row tiles for strip nt (fp16, accumulator layout)
+      floatx4 gam[2];
     };
     Ops A, B;
-    auto load_w = [&](Ops& X, rsrc_t r) {  // -W of this wave's chunk rows, Utilde tiles
-#pragma unroll
-      for (int j = 0; j < 4; ++j) X.wn[j] = ld_frag(r, frag_off, OFF_WN + (j * 4 + w) * 1024);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        X.ut[nt] = ld_tile(r, frag_off, OFF_UT + ((NT * sg + nt) * 4 + w) * 1024);
-    };
-    // e^{G_C} is only used in the update's final fma, which also needs Ktil^T: loaded
-    // together, they share one wait
-    auto load_kt = [&](Ops& X, rsrc_t r) {  // Ktil^T of this wave's key rows, e^{G_C}
+    auto load_ops = [&](Ops& X, rsrc_t r) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) X.kt[u][ks] = ld_frag(r, frag_off, OFF_KT + ((2 * w + u) * 2 + ks) * 1024);
+        for (int j = 0; j < 4; ++j) X.phi[u][j] = ld_frag(r, frag_off, OFF_PHI + ((2 * w + u) * 4 + j) * 1024);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, OFF_Z + ((NT * sg + nt) * 4 + w) * 1024);
 #pragma unroll
       for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
     };
@@ -808,6 +872,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // chunk reloads itself), unconditionally and in a fixed order, so the loop has no branch
     auto step = [&](Ops& X, int64_t c) {
       const rsrc_t rn = chunk_rsrc(c + 2);
+      const int bf = (int)(c & 1);
       // -- all-gather the state strips in fp16
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -816,61 +881,37 @@ __global__ __launch_bounds__(512) void rec_kernel(
           half4 hv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
-          *reinterpret_cast<half4*>(&sx[16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
+          *reinterpret_cast<half4*>(&sx[bf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
         }
       __syncthreads();
-      // -- U' = Utilde - W S for this wave's 16 chunk rows, all-gathered as fp16 hi + lo;
-      //    two independent accumulation chains over the four k-steps halve the latency
-      floatx4 U[NT], U2[NT];
+      // -- this wave's state rows: S = Diag(e^{G_C}) S + Z - Phi S, where Phi S runs as four
+      //    independent accumulation chains (two row tiles, two halves of the key range)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        U[nt] = mfma_f16(X.wn[0], state_frag(nt, 0), transition ? floatx4{0.f, 0.f, 0.f, 0.f} : X.ut[nt]);
-        U2[nt] = mfma_f16(X.wn[2], state_frag(nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
-        U[nt] = mfma_f16(X.wn[1], state_frag(nt, 1), U[nt]);
-        U2[nt] = mfma_f16(X.wn[3], state_frag(nt, 3), U2[nt]);
-        U[nt] += U2[nt];
-      }
-      load_w(X, rn);
+        half8 sf[4];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        half4 hh, ll;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          _Float16 a, bq;
-          split_f16(U[nt][i], a, bq);
-          hh[i] = a;
-          ll[i] = bq;
-        }
-        *reinterpret_cast<half4*>(&ux[0][16 * nt + nn][16 * w + 4 * gq]) = hh;
-        *reinterpret_cast<half4*>(&ux[1][16 * nt + nn][16 * w + 4 * gq]) = ll;
-      }
-      __syncthreads();
-      // -- this wave's state rows: S = Diag(e^{G_C}) S + Ktil^T U'
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        half8 uh[2], ul[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          uh[ks] = lds_frag(&ux[0][16 * nt + nn][32 * ks], gq);
-          ul[ks] = lds_frag(&ux[1][16 * nt + nn][32 * ks], gq);
-        }
-        floatx4 ah[2], al[2];  // hi and lo chains of both row tiles: four independent chains
+        for (int j = 0; j < 4; ++j) sf[j] = state_frag(bf, nt, j);
+        floatx4 a0[2], a1[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          ah[u] = mfma_f16(X.kt[u][0], uh[0], floatx4{0.f, 0.f, 0.f, 0.f});
-          al[u] = mfma_f16(X.kt[u][0], ul[0], floatx4{0.f, 0.f, 0.f, 0.f});
+          a0[u] = mfma_f16(X.phi[u][0], sf[0], floatx4{0.f, 0.f, 0.f, 0.f});
+          a1[u] = mfma_f16(X.phi[u][2], sf[2], floatx4{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          ah[u] = mfma_f16(X.kt[u][1], uh[1], ah[u]);
-          al[u] = mfma_f16(X.kt[u][1], ul[1], al[u]);
+          a0[u] = mfma_f16(X.phi[u][1], sf[1], a0[u]);
+          a1[u] = mfma_f16(X.phi[u][3], sf[3], a1[u]);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], ah[u][i] + al[u][i]);
+          for (int i = 0; i < 4; ++i) {
+            // the transition walk has V = 0, so Z = 0
+            const float zv = transition ? 0.f : static_cast<float>(X.z[nt][4 * u + i]);
+            s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], zv - (a0[u][i] + a1[u][i]));
+          }
       }
-      load_kt(X, rn);
+      load_ops(X, rn);
       // -- the state after every ckpt_chunks full chunks, if asked for
       if (ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * C <= si.len) {
         const int64_t slot = ck_base + (c + 1) / ck_every - 1;
@@ -886,11 +927,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
       }
     };
     if (c_end > c_lo) {
-      const rsrc_t r0 = chunk_rsrc(c_lo), r1 = chunk_rsrc(c_lo + 1);
-      load_w(A, r0);
-      load_kt(A, r0);
-      load_w(B, r1);
-      load_kt(B, r1);
+      load_ops(A, chunk_rsrc(c_lo));
+      load_ops(B, chunk_rsrc(c_lo + 1));
     }
     // Nothing may be pending on entry to the loop: the compiler computes the loop's memory
     // waits from the merge of its entry paths and the back edge, and loads left in flight on
@@ -914,10 +952,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
     }
   } else if (job.mode != REC_OUTPUT) {
     // ------------------------------------------------ no outputs: keep the barriers in step
-    for (int64_t c = c_lo; c < c_end; ++c) {
-      __syncthreads();
-      __syncthreads();
-    }
+    for (int64_t c = c_lo; c < c_end; ++c) __syncthreads();
   } else {
     // ------------------------------------------------ output waves: chunk rows 16w .. 16w+15
     const int row_stride = H * DV;  // elements between consecutive tokens
@@ -943,18 +978,18 @@ __global__ __launch_bounds__(512) void rec_kernel(
         X.oh[nt] = ld_tile(r, frag_off, OFF_OH + ((NT * sg + nt) * 4 + w) * 1024);
     };
     auto step = [&](Ops& X, int64_t c) {
+      const int bf = (int)(c & 1);
       __syncthreads();
-      // the products read the state before the second barrier (the state waves rewrite it
-      // after that barrier); the stores follow it, off the state waves' path
+      // the products read the state entering the chunk, from the buffer the state waves
+      // filled before this barrier
       floatx4 acc[NT], acc2[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = mfma_f16(X.qh[0], state_frag(nt, 0), X.oh[nt]);
-        acc2[nt] = mfma_f16(X.qh[2], state_frag(nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
-        acc[nt] = mfma_f16(X.qh[1], state_frag(nt, 1), acc[nt]);
-        acc2[nt] = mfma_f16(X.qh[3], state_frag(nt, 3), acc2[nt]);
+        acc[nt] = mfma_f16(X.qh[0], state_frag(bf, nt, 0), X.oh[nt]);
+        acc2[nt] = mfma_f16(X.qh[2], state_frag(bf, nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[nt] = mfma_f16(X.qh[1], state_frag(bf, nt, 1), acc[nt]);
+        acc2[nt] = mfma_f16(X.qh[3], state_frag(bf, nt, 3), acc2[nt]);
       }
-      __syncthreads();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
       load_q(X, c + 2);
