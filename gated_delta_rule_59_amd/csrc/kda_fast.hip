@@ -846,31 +846,41 @@ __global__ __launch_bounds__(512) void rec_kernel(
         }
 
     const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
-    // Operands are loaded two chunks ahead into two register sets used alternately (the
-    // loop is unrolled by two, so no set is ever copied): a chunk's loads have two chunks'
-    // time to arrive, which covers a first read of the workspace from HBM.
+    // Operands are loaded two chunks ahead into three register sets used in rotation (the
+    // loop is unrolled by three, so no set is ever copied): a chunk's loads have two chunks'
+    // time to arrive, which covers a first read of the workspace from HBM, and the set being
+    // filled is idle for the whole step, so its loads are spread over the step in three
+    // groups instead of leaving the vector memory unit one burst to drain while the chain
+    // waits behind it.
     struct Ops {
       half8 phi[2][4];  // Phi rows of key row tiles 2w + u, k-steps over keys
       half8 z[NT];      // Z of both key row tiles for strip nt (fp16, accumulator layout)
       floatx4 gam[2];
     };
-    Ops A, B;
+    Ops A, B, Cs;
+    auto load_part = [&](Ops& X, rsrc_t r, int part) {
+      if (part < 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X.phi[part][j] = ld_frag(r, frag_off, OFF_PHI + ((2 * w + part) * 4 + j) * 1024);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, OFF_Z + ((NT * sg + nt) * 4 + w) * 1024);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
+      }
+    };
     auto load_ops = [&](Ops& X, rsrc_t r) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) X.phi[u][j] = ld_frag(r, frag_off, OFF_PHI + ((2 * w + u) * 4 + j) * 1024);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, OFF_Z + ((NT * sg + nt) * 4 + w) * 1024);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
+      load_part(X, r, 0);
+      load_part(X, r, 1);
+      load_part(X, r, 2);
     };
     auto chunk_rsrc = [&](int64_t c) {
       return make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)kBlockBytes);
     };
-    // one chunk with operand set X; X is then reloaded for chunk c + 2 (past the end, the last
-    // chunk reloads itself), unconditionally and in a fixed order, so the loop has no branch
-    auto step = [&](Ops& X, int64_t c) {
+    // one chunk with operand set X, while set Y (idle since the previous chunk) is loaded with
+    // chunk c + 2 (past the end, the last chunk reloads itself), unconditionally and in a
+    // fixed order, so the loop has no branch
+    auto step = [&](Ops& X, Ops& Y, int64_t c) {
       const rsrc_t rn = chunk_rsrc(c + 2);
       const int bf = (int)(c & 1);
       // -- all-gather the state strips in fp16
@@ -883,6 +893,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
           *reinterpret_cast<half4*>(&sx[bf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
         }
+      load_part(Y, rn, 0);
       __syncthreads();
       // -- this wave's state rows: S = Diag(e^{G_C}) S + Z - Phi S, where Phi S runs as four
       //    independent accumulation chains (two row tiles, two halves of the key range)
@@ -891,6 +902,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
         half8 sf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) sf[j] = state_frag(bf, nt, j);
+        if (nt == 0) load_part(Y, rn, 1);
         floatx4 a0[2], a1[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -911,7 +923,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
             s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], zv - (a0[u][i] + a1[u][i]));
           }
       }
-      load_ops(X, rn);
+      load_part(Y, rn, 2);
       // -- the state after every ckpt_chunks full chunks, if asked for
       if (ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * C <= si.len) {
         const int64_t slot = ck_base + (c + 1) / ck_every - 1;
@@ -936,11 +948,13 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // full one.
     __builtin_amdgcn_s_waitcnt(0);
     int64_t c = c_lo;
-    for (; c + 1 < c_end; c += 2) {
-      step(A, c);
-      step(B, c + 1);
+    for (; c + 2 < c_end; c += 3) {
+      step(A, Cs, c);
+      step(B, A, c + 1);
+      step(Cs, B, c + 2);
     }
-    if (c < c_end) step(A, c);
+    if (c < c_end) step(A, Cs, c);
+    if (c + 1 < c_end) step(B, A, c + 1);
     if (S_T) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
