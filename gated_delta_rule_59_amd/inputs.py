@@ -15,6 +15,8 @@ Kimi K3 architecture page for the -5 floor on the per-step log-decay):
   3  varlen-16    16 packed sequences, lengths uniform in [512, 16384], H=32, dk=dv=128, bf16
   4  decode-512   N=512 sequences, H=32, dk=dv=128, fp32 state 0.02 N(0,1) (1 GiB), bf16 token
                   inputs, a pool of 16 seeded step-input sets cycled over the steps
+  5  unbounded-4k prefill-4k with g = -20 sigmoid(N(0,1)) (the decay-bound ablation's inputs)
+  6  long memory  g = f sigmoid(N(0,1)) for a small |f| (test cases: the carried state dominates)
 
 Every array is produced in float32 and then rounded to the storage dtype; the
 float32 arrays returned hold exactly the values the kernels receive.
@@ -214,4 +216,17 @@ def make_unbounded(T: int = 4096, H: int = 16, B: int = 1) -> KDAInputs:
     q, k, v, g, beta = draw_activations(key, B, T, H, 128, 128, "bf16", gate_floor=UNBOUNDED_FLOOR)
     S0 = draw_state(key, B, H, 128, 128)
     wl = Workload("unbounded-4k", 5, H, 128, 128, 64, "bf16", B=B, T=T, n_seq=B)
+    return KDAInputs(wl, q, k, v, g, beta, S0)
+
+
+def make_long_memory(gate_floor: float, T: int = 2048, H: int = 2, B: int = 1) -> KDAInputs:
+    """prefill-4k's distributions with a weak decay, g = gate_floor sigmoid(N(0,1)) for a small
+    |gate_floor| (e.g. -0.1 or -0.01): the state keeps most of itself across a 64-token chunk
+    (e^{-0.16} per chunk on average at -0.01), so what is carried from chunk to chunk, and
+    from segment to segment, dominates the outputs. (At the recipe's -5 the state entering a
+    chunk has decayed by about e^-160 before the chunk ends.)"""
+    key = (0, 6, int(round(-gate_floor * 1e4)))
+    q, k, v, g, beta = draw_activations(key, B, T, H, 128, 128, "bf16", gate_floor=gate_floor)
+    S0 = draw_state(key, B, H, 128, 128)
+    wl = Workload(f"long-memory g>={gate_floor}", 6, H, 128, 128, 64, "bf16", B=B, T=T, n_seq=B)
     return KDAInputs(wl, q, k, v, g, beta, S0)

@@ -47,6 +47,9 @@ CASES = {
     "no initial state": lambda: _no_s0(inputs.make_prefill(1, T=200, H=2)),
     "dense batch B=2 T=1093 H=3 (18 chunks, partial last)": lambda: batch_case(2, 1093, 3),
     "no initial state, 9 full chunks": lambda: _no_s0(batch_case(1, 9 * 64, 2)),
+    # weak decay: the state carried across chunks dominates the outputs
+    "long memory g>=-0.1 T=2048": lambda: inputs.make_long_memory(-0.1),
+    "long memory g>=-0.01 T=2048 B=2": lambda: inputs.make_long_memory(-0.01, B=2),
 }
 
 

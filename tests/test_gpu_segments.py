@@ -30,6 +30,8 @@ CASES = {
     "prefill-64k-bound T=2048 H=2": lambda: inputs.make_prefill(2, T=2048, H=2),
     "5 chunks (empty trailing segments)": lambda: inputs.make_prefill(1, T=300, H=2),
     "ragged varlen": ragged_case,
+    # weak decay: the segment transitions carry most of the state
+    "long memory g>=-0.01 T=2048": lambda: inputs.make_long_memory(-0.01),
 }
 
 
