@@ -17,7 +17,7 @@
 //    cumulative log-decay; A and Aqk on the matrix cores; the inverse (I + A)^{-1} by
 //    blocked forward substitution in LDS; then P, Qhat, Ohat, W, Utilde, Phi and Z on the
 //    matrix cores. Channel-major (transposed) operands come from products with an identity
-//    fragment, so no LDS staging array is needed and three workgroups fit one CU.
+//    fragment, so no LDS staging array is needed.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
 //    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
 //    and result tiles (1 KiB = 64 lanes x 4 fp32).
@@ -57,9 +57,6 @@ constexpr int OFF_Z = 49152;     // Z = Ktil^T Utilde, fp16 tiles in accumulator
 constexpr int OFF_OH = 81920;    // Ohat result tiles, fp32: [value tile (8)][row tile (4)]
 constexpr int OFF_GAM = 114688;  // e^{G_C}, fp32 [128]
 constexpr size_t kBlockBytes = 115200;
-// Ktil^T fragments [dk tile (8)][k-step over chunk rows (2)] are parked in the Z region while
-// a workgroup of the prep kernel builds its block (Z is written after they are read).
-constexpr int OFF_KTMP = OFF_Z;
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -143,14 +140,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
-// 8-byte workspace stores go through a buffer resource of the block: the lane's byte offset
-// is one VGPR and the constant part an SGPR, so no 64-bit address per store stays live.
-// 16-byte stores are global stores: a buffer store wider than 8 bytes with an SGPR offset
-// gets no wait state before its data registers are rewritten, and on gfx950 the last dword of
-// some lanes was then read after the rewrite (wrong workspace values, intermittently).
-__device__ __forceinline__ void st_half(rsrc_t r, int lane_off, int off, const half4& f) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f), r, lane_off, off, 0);
-}
+// Workspace stores of 16 bytes per lane are global stores: a buffer store wider than 8 bytes
+// with an SGPR offset gets no wait state before its data registers are rewritten, and on
+// gfx950 the last dword of some lanes was then read after the rewrite (wrong workspace values,
+// intermittently).
 
 // x from lane m - S of the same 16-lane DPP row (0 for m < S).
 template <int S>
@@ -221,17 +214,19 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 // generation (each e^{G_r - G_j} formed per pair and channel, in fp32 on the vector ALUs),
 // which needs no bound on the decay: the ablation that measures what the bound buys.
 template <bool PAIRWISE>
-__global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
+__global__ __launch_bounds__(256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
     int n_seq, uint8_t* __restrict__ ws, int c_lo, int c_span) {
   constexpr int AS = C + 4;  // row stride (fp32) of A and T
-  // One LDS arena reused phase by phase (byte ranges), 51.5 KB so that three workgroups share
-  // a CU:
+  // One LDS arena reused phase by phase (byte ranges), 66 KB, two workgroups per CU (the
+  // kernel needs about 190 registers; at three workgroups it spilled, and every spill reload
+  // waited for all loads in flight):
   //   tile products: lent column operands k cf, fp32 [3][4][64][8]     [0, 24576)
   //                  per-channel tables (tile totals and factors)     [24576, 32256)
   //                  Kbar^T fragments (kept until the last products)  [34816, 51200)
+  //                  Ktil^T fragments (kept until the last products)  [51200, 67584)
   //   inverse:       A fp32 [64][AS] [0, 17408), T [17408, 34816)
   //   products:      V fragments [0, 16384), once M and P are in registers
   // A fragment array holds 16 fragments [16-column tile][k-step over chunk rows], each in
@@ -239,8 +234,8 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   // The pairwise ablation first stages per wave G fp32 [16][132] and k, q bf16 [16][136].
   constexpr int PW_G = 16 * 132 * 4, PW_KQ = 16 * 136 * 2, PW_WAVE = PW_G + 2 * PW_KQ;
   constexpr int OFF_TAB = PAIRWISE ? 4 * PW_WAVE : 24576;
-  constexpr int OFF_KBF = 34816;
-  constexpr int ARENA = PAIRWISE ? OFF_TAB + 7680 : 51200;
+  constexpr int OFF_KBF = 34816, OFF_KTL = 51200;
+  constexpr int ARENA = PAIRWISE ? OFF_TAB + 7680 : 67584;
   __shared__ __align__(16) unsigned char arena[ARENA];
   __shared__ __align__(16) float Bs[C];
   float* KC = reinterpret_cast<float*>(arena);
@@ -249,10 +244,12 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   float(*ECH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 4096);
   float(*XCH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 6144);
   half8* KBF = reinterpret_cast<half8*>(arena + OFF_KBF);
+  half8* KTL = reinterpret_cast<half8*>(arena + OFF_KTL);
   float* A32 = reinterpret_cast<float*>(arena);
   float* T32 = reinterpret_cast<float*>(arena + 17408);
   half8* VBF = reinterpret_cast<half8*>(arena);
   static_assert(!PAIRWISE || OFF_TAB + 7680 <= ARENA, "layout");
+  static_assert(OFF_KTL + 16384 <= ARENA && (PAIRWISE || OFF_TAB + 7680 <= OFF_KBF), "layout");
   static_assert(4 * PW_WAVE <= (PAIRWISE ? ARENA : 1 << 30), "layout");
 
   const int h = blockIdx.x % H;
@@ -291,31 +288,44 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   uint16_t braw;
   const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
   {
+    // g first: the decay scan needs only g, and loads complete in the order they are issued,
+    // so the scan waits for a third of the bytes while k and q are still arriving. q of the
+    // last two k-steps is loaded during the tile products, two k-steps ahead of its use: at
+    // this point its registers would be spilled, and a spill waits for every load in flight.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int64_t e = erow + 32 * ks + 16 * hf + 4 * gq;
-        graw[ks][hf] = *reinterpret_cast<const u16x4*>(g + e);
-        kraw[ks][hf] = *reinterpret_cast<const u16x4*>(k + e);
-        qraw[ks][hf] = *reinterpret_cast<const u16x4*>(q + e);
-      }
+      for (int hf = 0; hf < 2; ++hf)
+        graw[ks][hf] = *reinterpret_cast<const u16x4*>(g + erow + 32 * ks + 16 * hf + 4 * gq);
     braw = beta[(tok0 + min(row, Cn - 1)) * H + h];
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        kraw[ks][hf] = *reinterpret_cast<const u16x4*>(k + erow + 32 * ks + 16 * hf + 4 * gq);
+#pragma unroll
+    for (int ks = 0; ks < (PAIRWISE ? 4 : 2); ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qraw[ks][hf] = *reinterpret_cast<const u16x4*>(q + erow + 32 * ks + 16 * hf + 4 * gq);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
-  float gs[4][8];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  //      (recomputed from the raw g in each phase that needs it: holding the 32 scanned values
+  //      would cost 16 more registers than the packed bf16 g through the whole kernel)
+  auto scan_ks = [&](int ks, float (&gk)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      gs[ks][i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
-  if (m == 15) {  // the tile's totals
+      gk[i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
+  };
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 4 * gq]) =
-          floatx4{gs[ks][0], gs[ks][1], gs[ks][2], gs[ks][3]};
-      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 16 + 4 * gq]) =
-          floatx4{gs[ks][4], gs[ks][5], gs[ks][6], gs[ks][7]};
+  for (int ks = 0; ks < 4; ++ks) {
+    float gk[8];
+    scan_ks(ks, gk);
+    if (m == 15) {  // the tile's totals
+      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 4 * gq]) = floatx4{gk[0], gk[1], gk[2], gk[3]};
+      *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 16 + 4 * gq]) = floatx4{gk[4], gk[5], gk[6], gk[7]};
     }
   }
   if (gq == 0) Bs[row] = row_ok ? bf16_bits_to_f32(braw) : 0.f;
@@ -351,15 +361,18 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     uint16_t* Qw = reinterpret_cast<uint16_t*>(arena + w * PW_WAVE + PW_G + PW_KQ);
     const u16x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      float gk[8];
+      scan_ks(ks, gk);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int c0 = 32 * ks + 16 * hf + 4 * gq;
         *reinterpret_cast<floatx4*>(&Gw[m * 132 + c0]) =
-            floatx4{gs[ks][4 * hf], gs[ks][4 * hf + 1], gs[ks][4 * hf + 2], gs[ks][4 * hf + 3]};
+            floatx4{gk[4 * hf], gk[4 * hf + 1], gk[4 * hf + 2], gk[4 * hf + 3]};
         *reinterpret_cast<u16x4*>(&Kw[m * 136 + c0]) = row_ok ? kraw[ks][hf] : zero4;
         *reinterpret_cast<u16x4*>(&Qw[m * 136 + c0]) = row_ok ? qraw[ks][hf] : zero4;
       }
+    }
     __syncthreads();
     for (int c = 0; c < DK; c += 4) {
       const floatx4 gr = *reinterpret_cast<const floatx4*>(&Gw[m * 132 + c]);
@@ -408,9 +421,11 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   };
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  // ---- column operands: k cf lent to later row tiles, and Ktil^T fragments (workspace)
+  // ---- column operands: k cf lent to later row tiles, and Ktil^T fragments (LDS)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    float gk[8];
+    scan_ks(ks, gk);
     floatx4 kc[2];
     half8 kt16;
 #pragma unroll
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
-        kc[hf][j] = kv * exp2_tile(tw[j] - gs[ks][4 * hf + j]);  // k e^{Gend_w - G_r}
+        kc[hf][j] = kv * exp2_tile(tw[j] - gk[4 * hf + j]);  // k e^{Gend_w - G_r}
         kt16[4 * hf + j] = static_cast<_Float16>(kc[hf][j] * ee[j]);
       }
     }
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      st_half(wsr, half_lane, OFF_KTMP + (2 * ks + hf) * 2048, to_half4(mfma_f16(kt16, idf[hf], zero)));
+      store_half_lds(reinterpret_cast<uint8_t*>(KTL), 2 * ks + hf, mfma_f16(kt16, idf[hf], zero));
   }
   __syncthreads();
   // ---- per k-step: row factors, Qbar, Kbar^T fragments (LDS), and the A and Aqk tiles of row
@@ -447,6 +462,13 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
   half8 qbar[4];  // Qbar as A-operand fragments of row tile w
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    if (!PAIRWISE && ks < 2) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qraw[ks + 2][hf] = *reinterpret_cast<const u16x4*>(q + erow + 32 * (ks + 2) + 16 * hf + 4 * gq);
+    }
+    float gk[8];
+    scan_ks(ks, gk);
     float kr[8], qr[8], kd[8];
     half8 kb16;
 #pragma unroll
@@ -457,7 +479,7 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
         const int i = 4 * hf + j;
         const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
         const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
-        const float rf = exp2_tile(gs[ks][i]);  // e^{G_r - ref_w}
+        const float rf = exp2_tile(gk[i]);  // e^{G_r - ref_w}
         kr[i] = kv * rf;
         qr[i] = qv * rf;
         kd[i] = kv * __builtin_amdgcn_rcpf(rf);
@@ -694,14 +716,6 @@ __global__ __launch_bounds__(256, PAIRWISE ? 2 : 3) void prep_kernel(
       }
     }
   }
-  __syncthreads();  // T is dead: Ktil^T fragments are copied from the workspace into its place
-  half8* KTL = reinterpret_cast<half8*>(arena + 17408);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int f = t + 256 * e;  // 16-byte unit of the 16 KiB fragment array
-    KTL[f] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(wsr, f * 16, OFF_KTMP, 0));
-  }
-  __syncthreads();
   // ---- Phi = Ktil^T W for key rows kt and key columns 32w .. 32w + 31, computed as
   //      Phi^T = W^T Ktil so that each lane ends with its own row: A-operand fragments (kt, w)
 #pragma unroll
