@@ -312,12 +312,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
-  //      (recomputed from the raw g in each phase that needs it: holding the 32 scanned values
-  //      would cost 16 more registers than the packed bf16 g through the whole kernel)
-  auto scan_ks = [&](int ks, float (&gk)[8]) {
+  float gsa[4][8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      gk[i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
+      gsa[ks][i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
+  auto scan_ks = [&](int ks, float (&gk)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gk[i] = gsa[ks][i];
   };
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
