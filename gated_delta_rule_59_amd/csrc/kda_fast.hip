@@ -788,6 +788,8 @@ constexpr int kMaxJobs = 16;
 struct RecJobs {
   RecJob job[kMaxJobs];
   int64_t blocks_per_job;
+  int halves;  // 2: two workgroups per strip run the same state walk, each with the outputs of
+               // half of the chunk rows (fewer operand bytes per CU when CUs would be idle)
 };
 
 template <typename TOut, int NT>
@@ -816,8 +818,9 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // XCD-aware placement: the strip groups of one (sequence, head) share an XCD and its L2.
   const int b = (int)(blockIdx.x % jobs.blocks_per_job);
   const int xcd = b & 7, rest = b >> 3;
-  const int sg = rest % NG;
-  const int64_t pair = (int64_t)(rest / NG) * 8 + xcd;
+  const int sg = rest % NG, r2 = rest / NG;
+  const int half = r2 % jobs.halves;
+  const int64_t pair = (int64_t)(r2 / jobs.halves) * 8 + xcd;
   if (pair >= (int64_t)n_seq * H) return;
   const int n = (int)(pair / H), h = (int)(pair % H);
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
@@ -838,7 +841,9 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
   const int64_t ck_base =
       ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
-  const int ck_every = job.mode == REC_OUTPUT ? ckpt_chunks : 0;
+  // the second workgroup of a split pair repeats the walk: only the first writes states
+  const int ck_every = job.mode == REC_OUTPUT && half == 0 ? ckpt_chunks : 0;
+  if (half != 0) S_T = nullptr;
 
   if (wave < 4) {
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
@@ -980,7 +985,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i)
             S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
     }
-  } else if (job.mode != REC_OUTPUT) {
+  } else if (job.mode != REC_OUTPUT || (w >> 1) % jobs.halves != half) {
     // ------------------------------------------------ no outputs: keep the barriers in step
     for (int64_t c = c_lo; c < c_end; ++c) __syncthreads();
   } else {
@@ -1121,10 +1126,11 @@ size_t fast_workspace_bytes(const ChunkPlan& p) {
 namespace {
 
 template <typename TOut>
-hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int64_t pairs,
+hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int halves, int64_t pairs,
                       RecJobs jobs, int n_jobs, const int32_t* chunk_off,
                       const int32_t* ckpt_off, uint8_t* ws) {
-  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP);
+  jobs.halves = halves;
+  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP) * halves;
   const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
   const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
   auto kern = two ? rec_kernel<TOut, 2> : rec_kernel<TOut, 1>;
@@ -1169,15 +1175,19 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   const bool two = pairs * NSTRIP >= 4LL * n_cu;
   hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
   if (e != hipSuccess) return e;
-  auto rec = [&](const RecJobs& jobs, int n_jobs) {
-    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws)
-                      : launch_rec<float>(p, stream, two, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws);
+  auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
+    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws)
+                      : launch_rec<float>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws);
   };
   RecJobs jobs = {};
   const int P = n_segments(p);
   if (P == 1) {  // one walk over every chunk
     jobs.job[0] = RecJob{0, INT64_MAX, p.S0, p.S_T, REC_OUTPUT};
-    return rec(jobs, 1);
+    // The walk is bound by each CU's vector memory unit (the operand bytes per chunk). When
+    // the strip workgroups leave at least half of the CUs idle, two workgroups per strip run
+    // the same state walk and split the output rows, so each loads the state operands and
+    // half of the output operands.
+    return rec(jobs, 1, !two && pairs * NSTRIP * 2 <= n_cu ? 2 : 1);
   }
   // Segmented walk (sequence split of the transition form): the chunks of each sequence are
   // cut at b_1 < ... < b_{P-1}. Pass 1 walks segment 0 from S0 (its exit is segment 1's entry)
@@ -1196,7 +1206,7 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     jobs.job[n++] = RecJob{q * span, (q + 1) * span, nullptr, summ(q), REC_SUMMARY};
     jobs.job[n++] = RecJob{q * span, (q + 1) * span, nullptr, trans(q), REC_TRANSITION};
   }
-  if ((e = rec(jobs, n)) != hipSuccess) return e;
+  if ((e = rec(jobs, n, 1)) != hipSuccess) return e;
   for (int q = 1; q <= P - 2; ++q) {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(pairs * NSTRIP)), dim3(256), 0, stream,
                        trans(q), entry(q), summ(q), entry(q + 1), pairs);
@@ -1206,7 +1216,7 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   for (int q = 1; q <= P - 1; ++q)
     jobs.job[n++] = RecJob{q * span, q == P - 1 ? INT64_MAX : (q + 1) * span, entry(q),
                            q == P - 1 ? p.S_T : nullptr, REC_OUTPUT};
-  return rec(jobs, n);
+  return rec(jobs, n, 1);
 }
 
 }  // namespace kda
