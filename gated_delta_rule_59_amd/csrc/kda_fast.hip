@@ -5,17 +5,20 @@
 //   U' = M (V - Kbar S) = Utilde - W S,   M = (I + A)^{-1} diag(b),  W = M Kbar,  Utilde = M V
 //   A[r][j] = b_r sum_c k_r k_j e^{G_r - G_j} (j < r),   Aqk[r][j] = sum_c q_r k_j e^{G_r - G_j} (j <= r)
 //   O  = Qbar S + Aqk U' = Qhat S + Ohat,   Qhat = Qbar - P Kbar,   Ohat = P V,   P = Aqk M
-//   S <- Diag(e^{G_C}) S + Ktil^T U' = Diag(e^{G_C}) S + Z - Phi S,   Phi = Ktil^T W,  Z = Ktil^T Utilde
+//   S <- Diag(e^{G_C}) S + Ktil^T U' = Diag(e^{G_C}) S + Z - Phi S = S + Z + Psi S,
+//   Phi = Ktil^T W,  Z = Ktil^T Utilde,  Psi = -Phi - Diag(1 - e^{G_C})
 // with Kbar = K e^{G}, Qbar = Q e^{G}, Ktil = K e^{G_C - G}. Everything that does not depend on
-// the entry state (Phi, Z, Qhat, Ohat) is formed for all chunks in parallel; the serial walk
-// over the chunks then needs two products with the state per chunk (Phi S for the update,
+// the entry state (Psi, Z, Qhat, Ohat) is formed for all chunks in parallel; the serial walk
+// over the chunks then needs two products with the state per chunk (Psi S for the update,
 // Qhat S for the outputs), both of the state as it enters the chunk, so one exchange of the
-// state between waves per chunk suffices.
+// state between waves per chunk suffices. Folding the decay into Psi (fp16) costs no
+// precision where it matters: the stored diagonal term is 1 - e^{G_C}, small exactly when the
+// state is carried over many chunks, while the carried state itself stays in fp32.
 //
 // Two kernels.
 //  prep_kernel (one workgroup per chunk and head, all chunks in parallel): the per-channel
 //    cumulative log-decay; A and Aqk on the matrix cores; the inverse (I + A)^{-1} by
-//    blocked forward substitution in LDS; then P, Qhat, Ohat, W, Utilde, Phi and Z on the
+//    blocked forward substitution in LDS; then P, Qhat, Ohat, W, Utilde, Psi and Z on the
 //    matrix cores. Channel-major (transposed) operands come from products with an identity
 //    fragment, so no LDS staging array is needed.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
@@ -32,7 +35,7 @@
 //  rec_kernel (one workgroup per sequence, head and 16 value columns, serial over chunks):
 //    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence.
 //    Eight waves in two roles. Waves 0-3 own 32 key rows of the state each and carry the
-//    dependency chain: S <- Diag(e^{G_C}) S + Z - Phi S for their rows. Waves 4-7 compute the
+//    dependency chain: S <- S + Z + Psi S for their rows. Waves 4-7 compute the
 //    outputs Qhat S + Ohat of their 16 chunk rows from the same gathered state, off the chain.
 //    Columns of S evolve independently (the transition acts on the key side only), so
 //    splitting the value columns over workgroups is exact.
@@ -50,13 +53,12 @@ constexpr int NSTRIP = DV / 16;  // 16-column strips per (sequence, head)
 
 // Workspace block of one (chunk, head), byte offsets. Fragment f of a group starts at
 // group + f * 1024 (lane l's eight fp16 at + l * 16); result tile f likewise (four fp32).
-constexpr int OFF_PHI = 0;       // Phi = Ktil^T W as A operand: [key row tile (8)][k-step over keys (4)]
+constexpr int OFF_PHI = 0;       // Psi as A operand: [key row tile (8)][k-step over keys (4)]
 constexpr int OFF_QH = 32768;    // Qhat as A operand: [k-step over dk (4)][row tile (4)]
 constexpr int OFF_Z = 49152;     // Z = Ktil^T Utilde, fp16 tiles in accumulator layout:
                                  //   [value tile (8)][key row pair (4)][lane][tile of the pair][4]
 constexpr int OFF_OH = 81920;    // Ohat result tiles, fp32: [value tile (8)][row tile (4)]
-constexpr int OFF_GAM = 114688;  // e^{G_C}, fp32 [128]
-constexpr size_t kBlockBytes = 115200;
+constexpr size_t kBlockBytes = 114688;
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   constexpr int ARENA = PAIRWISE ? OFF_TAB + 7680 : 67584;
   __shared__ __align__(16) unsigned char arena[ARENA];
   __shared__ __align__(16) float Bs[C];
+  __shared__ float GAMS[DK];  // e^{G_C} per key channel, for the diagonal of Psi
   float* KC = reinterpret_cast<float*>(arena);
   float(*TOT)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB);
   float(*PCH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 2048);
@@ -274,7 +277,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   const int64_t tok0 = si.tok0 + c_in * C;
   const int Cn = (int)min((int64_t)C, si.len - c_in * C);
   uint8_t* blk = ws + ((size_t)(si.cid0 + c_in) * H + h) * kBlockBytes;
-  const rsrc_t wsr = make_rsrc(blk, (int64_t)kBlockBytes);
 
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     if (hf == 0) {
       XCH[0][c] = exp2f(t1);       // column factor of block (2, 0): e^{ref_2 - Gend_0}
       XCH[1][c] = exp2f(t1 + t2);  // (3, 0)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(exp2f(gc)), wsr, c * 4, OFF_GAM, 0);
+      GAMS[c] = exp2f(gc);
     } else {
       XCH[2][c] = exp2f(t2);       // (3, 1)
     }
@@ -729,11 +731,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       d0 = mfma_f16(wb[0][kk], ktf, d0);
       d1 = mfma_f16(wb[1][kk], ktf, d1);
     }
+    // Psi = -Phi - Diag(1 - e^{G_C}): the diagonal entry of row 16 kt + m sits in k-step
+    // kt / 2, in the lanes with gq = m / 4, slot (m mod 4) + 4 (kt mod 2)
+    const int dslot = (kt >> 1) == w && gq == (m >> 2) ? (m & 3) + 4 * (kt & 1) : -1;
+    const float dlt = dslot >= 0 ? 1.f - GAMS[16 * kt + m] : 0.f;
     half8 ph;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ph[i] = static_cast<_Float16>(d0[i]);
-      ph[i + 4] = static_cast<_Float16>(d1[i]);
+      ph[i] = static_cast<_Float16>(-d0[i] - (i == dslot ? dlt : 0.f));
+      ph[i + 4] = static_cast<_Float16>(-d1[i] - (i + 4 == dslot ? dlt : 0.f));
     }
     *reinterpret_cast<half8*>(blk + OFF_PHI + (kt * 4 + w) * 1024 + l * 16) = ph;
   }
@@ -801,7 +807,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // blockIdx.x = job * blocks_per_job + (block within the job)
   // A workgroup owns NT strips of 16 value columns. One fp16 exchange per chunk through LDS,
   // followed by one barrier: the state strips entering the chunk (all 128 key rows), which the
-  // state waves need whole for Phi S and the output waves for Qhat S. They are stored
+  // state waves need whole for Psi S and the output waves for Qhat S. They are stored
   // column-major ([column][row]) so the rows a lane needs for a B operand are contiguous, with
   // rows padded by 8 halves against bank conflicts, in two buffers used by alternate chunks:
   // the buffer of chunk c is read between barrier c and barrier c + 1, and written again only
@@ -866,7 +872,6 @@ __global__ __launch_bounds__(512) void rec_kernel(
                                    : (S0 ? S0[s_base + (int64_t)r * DV + col[nt]] : 0.f);
         }
 
-    const int gam_off = OFF_GAM + (32 * w + 4 * gq) * 4;
     // Operands are loaded two chunks ahead into three register sets used in rotation (the
     // loop is unrolled by three, so no set is ever copied): a chunk's loads have two chunks'
     // time to arrive, which covers a first read of the workspace from HBM, and the set being
@@ -874,9 +879,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // groups instead of leaving the vector memory unit one burst to drain while the chain
     // waits behind it.
     struct Ops {
-      half8 phi[2][4];  // Phi rows of key row tiles 2w + u, k-steps over keys
+      half8 phi[2][4];  // Psi rows of key row tiles 2w + u, k-steps over keys
       half8 z[NT];      // Z of both key row tiles for strip nt (fp16, accumulator layout)
-      floatx4 gam[2];
     };
     Ops A, B, Cs;
     auto load_part = [&](Ops& X, rsrc_t r, int part) {
@@ -886,8 +890,6 @@ __global__ __launch_bounds__(512) void rec_kernel(
       } else {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, OFF_Z + ((NT * sg + nt) * 4 + w) * 1024);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) X.gam[u] = ld_tile(r, gam_off, 64 * u);
       }
     };
     auto load_ops = [&](Ops& X, rsrc_t r) {
@@ -916,7 +918,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
         }
       load_part(Y, rn, 0);
       __syncthreads();
-      // -- this wave's state rows: S = Diag(e^{G_C}) S + Z - Phi S, where Phi S runs as four
+      // -- this wave's state rows: S = S + Z + Psi S, where Psi S runs as four
       //    independent accumulation chains (two row tiles, two halves of the key range)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i) {
             // the transition walk has V = 0, so Z = 0
             const float zv = transition ? 0.f : static_cast<float>(X.z[nt][4 * u + i]);
-            s[nt][u][i] = fmaf(X.gam[u][i], s[nt][u][i], zv - (a0[u][i] + a1[u][i]));
+            s[nt][u][i] += zv + (a0[u][i] + a1[u][i]);
           }
       }
       load_part(Y, rn, 2);
