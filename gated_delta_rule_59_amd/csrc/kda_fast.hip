@@ -906,6 +906,15 @@ __global__ __launch_bounds__(512) void rec_kernel(
     auto step = [&](Ops& X, Ops& Y, int64_t c) {
       const rsrc_t rn = chunk_rsrc(c + 2);
       const int bf = (int)(c & 1);
+      // S + Z seeds the accumulators, off the chain (the transition walk has V = 0, so Z = 0)
+      floatx4 seed[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            seed[nt][u][i] = s[nt][u][i] + (transition ? 0.f : static_cast<float>(X.z[nt][4 * u + i]));
       // -- all-gather the state strips in fp16
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -929,7 +938,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
         floatx4 a0[2], a1[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          a0[u] = mfma_f16(X.phi[u][0], sf[0], floatx4{0.f, 0.f, 0.f, 0.f});
+          a0[u] = mfma_f16(X.phi[u][0], sf[0], seed[nt][u]);
           a1[u] = mfma_f16(X.phi[u][2], sf[2], floatx4{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
@@ -938,13 +947,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
           a1[u] = mfma_f16(X.phi[u][3], sf[3], a1[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // the transition walk has V = 0, so Z = 0
-            const float zv = transition ? 0.f : static_cast<float>(X.z[nt][4 * u + i]);
-            s[nt][u][i] += zv + (a0[u][i] + a1[u][i]);
-          }
+        for (int u = 0; u < 2; ++u) s[nt][u] = a0[u] + a1[u];
       }
       load_part(Y, rn, 2);
       // -- the state after every ckpt_chunks full chunks, if asked for
