@@ -4,8 +4,9 @@
 
 A step is one kda_chunk_fwd (prefill: cumulative decay, tile products, the (I + A)
 inverse, state propagation and outputs) over one batch of the workload, inputs already
-resident on the GPU. K steps are timed between two device synchronisations; every launch
-is also bracketed by HIP events on the stream it runs on. A further --cold-steps launches
+resident on the GPU. K steps are timed between two device synchronisations, and bracketed
+as a whole by a pair of HIP events on the stream they run on (the average launch duration is
+the event time over K; no event sits between launches). A further --cold-steps launches
 are timed one by one after a cache flush each (secondary figure). The decode half of the metric
 (GB/s against HBM peak) is measured in the same run on the decode workload (N=512
 sequences, H=32, 1 GiB fp32 state updated in place), from its own timed loop.
@@ -70,22 +71,22 @@ def read_traffic(profile_name, kernel_hash):
 
 
 def time_launches(fn, steps, warmup, stream):
-    """Run fn() warmup times, then `steps` times with an event pair around each launch.
-    Returns (wall seconds for the timed steps, list of per-launch ms)."""
+    """Run fn() warmup times, then `steps` times between two synchronisations, with one HIP
+    event pair on `stream` around all of them. Returns (wall seconds for the timed steps,
+    average ms per launch from the events)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, a.elapsed_time(b) / steps
 
 
 def time_cold(fn, steps, stream, flush_bytes=512 << 20):
@@ -147,7 +148,7 @@ def bench_segments(stream, warmup, steps=10):
                                                         workspace=ws, stream=stream,
                                                         segments=P), steps, max(2, warmup // 4),
                               stream)
-        out[f"segments_{P}_event_ms" if P else "sequential_event_ms"] = sum(ms) / len(ms)
+        out[f"segments_{P}_event_ms" if P else "sequential_event_ms"] = ms
     out["tokens_per_s_best"] = 65536 / (min(v for kk, v in out.items() if kk.endswith("_ms")) * 1e-3)
     return out
 
@@ -166,8 +167,7 @@ def bench_decode(steps, warmup, stream):
         binding.decode_step(*pool[it[0] % inputs.DECODE_POOL], S, o=o, stream=stream)
         it[0] += 1
 
-    wall, ms = time_launches(step, steps, warmup, stream)
-    per = sum(ms) / len(ms)
+    wall, per = time_launches(step, steps, warmup, stream)
     nbytes = N * H * (2 * 4 * d * d + 2 * (4 * d + 1) + 4 * d)  # state in+out, inputs, fp32 o
 
     # speculative decoding on the same state: 4 draft tokens per sequence evaluated from one
@@ -183,7 +183,7 @@ def bench_decode(steps, warmup, stream):
     _, ms_c = time_launches(lambda: binding.decode_multi(*drafts, S, accept=acc,
                                                          want_output=False, stream=stream),
                             n_sp, 3, stream)
-    v_ms, c_ms = sum(ms_v) / len(ms_v), sum(ms_c) / len(ms_c)
+    v_ms, c_ms = ms_v, ms_c
     in_b = N * m * H * 2 * (4 * d + 1)
     spec = {"m": m, "verify_ms": v_ms, "verify_tokens_per_s": N * m / (v_ms * 1e-3),
             "verify_GB_per_s": (N * H * 4 * d * d + in_b + N * m * H * 4 * d) / (v_ms * 1e-3) / 1e9,
@@ -254,8 +254,7 @@ def main():
     def step():
         binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T, workspace=ws, stream=stream)
 
-    wall, ms = time_launches(step, args.steps, args.warmup, stream)
-    per_ms = sum(ms) / len(ms)
+    wall, per_ms = time_launches(step, args.steps, args.warmup, stream)
     cold = time_cold(step, args.cold_steps, stream) if args.cold_steps else None
     # the same launch also storing the state every 512 tokens (sparse checkpoints)
     ck_every = 512
@@ -267,15 +266,13 @@ def main():
         binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T, workspace=ws, stream=stream,
                           ckpt=ck, ckpt_every=ck_every)
 
-    _, ms_ck = time_launches(step_ck, max(10, args.steps // 4), 3, stream)
-    ck_ms = sum(ms_ck) / len(ms_ck)
+    _, ck_ms = time_launches(step_ck, max(10, args.steps // 4), 3, stream)
     # ablation: the same launch with the diagonal tiles evaluated pairwise (what the decay
     # bound's dense diagonal tiles save)
-    _, ms_pw = time_launches(lambda: binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T,
+    _, pw_ms = time_launches(lambda: binding.chunk_fwd(q, k, v, g, beta, S0, cu, o=o, S_T=S_T,
                                                        workspace=ws, stream=stream,
                                                        pairwise_diag=True),
                              max(10, args.steps // 4), 3, stream)
-    pw_ms = sum(ms_pw) / len(ms_pw)
     token_heads = B * T * H
     flops = flops_per_token_head() * token_heads
     nbytes = bytes_per_token_head() * token_heads + 2 * 4 * d * d * n_seq * H

@@ -139,10 +139,11 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
   kda::ChunkPlan p;
   kda_status s = validate_chunk_shapes(a, &p);
   if (s != KDA_OK) return s;
-  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)
-    return fail(KDA_ERR_NULL_PTR, "q, k, v, g, beta and o must be non-NULL");
   const size_t es = dsize(a->act_dtype), os = dsize(a->out_dtype);
   const size_t tok = (size_t)a->B * a->T * a->H;
+  // zero tokens: the per-token arrays are empty and may be NULL (as an empty tensor's is)
+  if (tok > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
+    return fail(KDA_ERR_NULL_PTR, "q, k, v, g, beta and o must be non-NULL");
   const size_t st = (size_t)p.n_seq * a->H * a->dk * a->dv * 4;
   const Range in[] = {range("q", a->q, tok * a->dk * es), range("k", a->k, tok * a->dk * es),
                       range("v", a->v, tok * a->dv * es), range("g", a->g, tok * a->dk * es),

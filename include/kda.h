@@ -69,7 +69,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Arguments of kda_chunk_fwd (prefill).
  *
  *   B, T       dense batch: B sequences of T tokens each. With cu_seqlens: B must be 1 and
- *              T is the packed total length.
+ *              T is the packed total length. T = 0 is allowed: no token is read or written
+ *              (q, k, v, g, beta and o may then be NULL) and S_T receives S0 (zeros if NULL).
  *   H          heads (independent).
  *   dk, dv     key and value head dims, each in {32, 64, 128}.
  *   chunk      chunk length in {16, 32, 64}; a performance knob (results agree across

@@ -180,3 +180,24 @@ def test_workload_varlen_full():
     o, s = run(x)
     assert np.isfinite(o).all()
     _chains_parity(x, o, s, [(n, (5 * n + 3) % x.wl.H) for n in range(x.wl.n_seq)], "varlen-16")
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_zero_tokens_carry_the_state(generic):
+    """T = 0: no token is read or written (the empty tensors' pointers are NULL) and the final
+    state is the initial one, bitwise; zeros without S0; in place as well."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    B, H = 2, 3
+    q, k, v, g, beta = (torch.empty((B, 0, H, 128), dtype=torch.bfloat16, device="cuda")
+                        for _ in range(5))
+    beta = torch.empty((B, 0, H), dtype=torch.bfloat16, device="cuda")
+    S0 = torch.from_numpy(inputs.draw_state((9, 7), B, H, 128, 128)).to("cuda")
+    o, s = binding.chunk_fwd(q, k, v, g, beta, S0, generic=generic)
+    _, z = binding.chunk_fwd(q, k, v, g, beta, None, generic=generic)
+    S = S0.clone()
+    binding.chunk_fwd(q, k, v, g, beta, S, S_T=S, generic=generic)
+    torch.cuda.synchronize()
+    assert o.shape == (B, 0, H, 128)
+    assert torch.equal(s, S0) and torch.equal(S, S0)
+    assert not z.any()
