@@ -282,12 +282,21 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l = t & 63, gq = l >> 4, m = l & 15;
   const int row = 16 * w + m;
-  const bool row_ok = row < Cn;
 
-  // ---- this lane's 32 elements of row 16w + m of k, q, g, v (rows past the end read as 0)
+  // ---- this lane's 32 elements of row 16w + m of k, q, g, v. The loads go through buffer
+  //      resources that end after the chunk's last valid row, so rows past the end read as
+  //      zero (k = q = v = 0, g = 0: decay 1, beta = 0) with no mask on the values.
   u16x4 kraw[4][2], qraw[4][2], graw[4][2], vraw[4][2];
   uint16_t braw;
-  const int64_t erow = ((tok0 + min(row, Cn - 1)) * H + h) * DK;
+  const int64_t tok_elems = (int64_t)H * DK;  // elements between consecutive tokens
+  const int64_t e0 = (tok0 * H + h) * DK;
+  const int64_t valid = ((int64_t)(Cn - 1) * tok_elems + DK) * 2;
+  const rsrc_t rs_q = make_rsrc(q + e0, valid), rs_k = make_rsrc(k + e0, valid),
+               rs_g = make_rsrc(g + e0, valid), rs_v = make_rsrc(v + e0, valid);
+  const int in_off = (int)((row * tok_elems + 4 * gq) * 2);
+  auto ld_in = [&](rsrc_t r, int ks, int hf) {
+    return __builtin_bit_cast(u16x4, __builtin_amdgcn_raw_buffer_load_b64(r, in_off, (32 * ks + 16 * hf) * 2, 0));
+  };
   {
     // g first: the decay scan needs only g, and loads complete in the order they are issued,
     // so the scan waits for a third of the bytes while k and q are still arriving. q of the
@@ -297,19 +306,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        graw[ks][hf] = *reinterpret_cast<const u16x4*>(g + erow + 32 * ks + 16 * hf + 4 * gq);
-    braw = beta[(tok0 + min(row, Cn - 1)) * H + h];
+        graw[ks][hf] = ld_in(rs_g, ks, hf);
+    braw = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(beta + tok0 * H + h, ((int64_t)(Cn - 1) * H + 1) * 2),
+                                                row * H * 2, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        kraw[ks][hf] = *reinterpret_cast<const u16x4*>(k + erow + 32 * ks + 16 * hf + 4 * gq);
+        kraw[ks][hf] = ld_in(rs_k, ks, hf);
 #pragma unroll
     for (int ks = 0; ks < (PAIRWISE ? 4 : 2); ++ks)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        qraw[ks][hf] = *reinterpret_cast<const u16x4*>(q + erow + 32 * ks + 16 * hf + 4 * gq);
+        qraw[ks][hf] = ld_in(rs_q, ks, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      gsa[ks][i] = row_scan(row_ok ? bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e : 0.f);
+      gsa[ks][i] = row_scan(bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e);
   auto scan_ks = [&](int ks, float (&gk)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) gk[i] = gsa[ks][i];
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       *reinterpret_cast<floatx4*>(&TOT[w][32 * ks + 16 + 4 * gq]) = floatx4{gk[4], gk[5], gk[6], gk[7]};
     }
   }
-  if (gq == 0) Bs[row] = row_ok ? bf16_bits_to_f32(braw) : 0.f;
+  if (gq == 0) Bs[row] = bf16_bits_to_f32(braw);
   __syncthreads();
   // ---- per-channel constants from the tile totals (half the threads per pair of tiles)
   {
@@ -363,7 +373,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     float* Gw = reinterpret_cast<float*>(arena + w * PW_WAVE);
     uint16_t* Kw = reinterpret_cast<uint16_t*>(arena + w * PW_WAVE + PW_G);
     uint16_t* Qw = reinterpret_cast<uint16_t*>(arena + w * PW_WAVE + PW_G + PW_KQ);
-    const u16x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float gk[8];
@@ -373,8 +382,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         const int c0 = 32 * ks + 16 * hf + 4 * gq;
         *reinterpret_cast<floatx4*>(&Gw[m * 132 + c0]) =
             floatx4{gk[4 * hf], gk[4 * hf + 1], gk[4 * hf + 2], gk[4 * hf + 3]};
-        *reinterpret_cast<u16x4*>(&Kw[m * 136 + c0]) = row_ok ? kraw[ks][hf] : zero4;
-        *reinterpret_cast<u16x4*>(&Qw[m * 136 + c0]) = row_ok ? qraw[ks][hf] : zero4;
+        *reinterpret_cast<u16x4*>(&Kw[m * 136 + c0]) = kraw[ks][hf];
+        *reinterpret_cast<u16x4*>(&Qw[m * 136 + c0]) = qraw[ks][hf];
       }
     }
     __syncthreads();
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       const floatx4 ee = *reinterpret_cast<const floatx4*>(&ECH[w][c0]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
+        const float kv = bf16_bits_to_f32(kraw[ks][hf][j]);
         kc[hf][j] = kv * exp2_tile(tw[j] - gk[4 * hf + j]);  // k e^{Gend_w - G_r}
         kt16[4 * hf + j] = static_cast<_Float16>(kc[hf][j] * ee[j]);
       }
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     if (!PAIRWISE && ks < 2) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        qraw[ks + 2][hf] = *reinterpret_cast<const u16x4*>(q + erow + 32 * (ks + 2) + 16 * hf + 4 * gq);
+        qraw[ks + 2][hf] = ld_in(rs_q, ks + 2, hf);
     }
     float gk[8];
     scan_ks(ks, gk);
@@ -481,8 +490,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * hf + j;
-        const float kv = row_ok ? bf16_bits_to_f32(kraw[ks][hf][j]) : 0.f;
-        const float qv = row_ok ? bf16_bits_to_f32(qraw[ks][hf][j]) : 0.f;
+        const float kv = bf16_bits_to_f32(kraw[ks][hf][j]);
+        const float qv = bf16_bits_to_f32(qraw[ks][hf][j]);
         const float rf = exp2_tile(gk[i]);  // e^{G_r - ref_w}
         kr[i] = kv * rf;
         qr[i] = qv * rf;
@@ -541,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      vraw[ks][hf] = *reinterpret_cast<const u16x4*>(v + erow + 32 * ks + 16 * hf + 4 * gq);
+      vraw[ks][hf] = ld_in(rs_v, ks, hf);
   __syncthreads();  // the lent operands and the tables are dead: A and T take the arena
   // ---- beta-scaled A rows into LDS (entries on or above the diagonal are never read);
   //      Aqk (lower, diagonal included) as A-operand fragments hi + lo in registers
@@ -649,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     half8 v16;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      v16[i] = static_cast<_Float16>(row_ok ? bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]) : 0.f);
+      v16[i] = static_cast<_Float16>(bf16_bits_to_f32(vraw[ks][i >> 2][i & 3]));
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
       store_half_lds(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
