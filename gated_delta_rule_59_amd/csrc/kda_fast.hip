@@ -1184,9 +1184,10 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
-  // workgroup maximises parallelism. Many pairs (at least four strip workgroups per CU): two
-  // strips per workgroup halve the operand traffic per column.
-  const bool two = pairs * NSTRIP >= 4LL * n_cu;
+  // workgroup maximises parallelism. At least one strip per CU: two strips per workgroup halve
+  // the state operand traffic per column (the walk is bound by each CU's vector memory unit);
+  // measured faster from one strip per CU on (prefill-64k-bound -1.5 %).
+  const bool two = pairs * NSTRIP >= (int64_t)n_cu;
   hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
@@ -1198,10 +1199,11 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   if (P == 1) {  // one walk over every chunk
     jobs.job[0] = RecJob{0, INT64_MAX, p.S0, p.S_T, REC_OUTPUT};
     // The walk is bound by each CU's vector memory unit (the operand bytes per chunk). When
-    // the strip workgroups leave at least half of the CUs idle, two workgroups per strip run
-    // the same state walk and split the output rows, so each loads the state operands and
-    // half of the output operands.
-    return rec(jobs, 1, !two && pairs * NSTRIP * 2 <= n_cu ? 2 : 1);
+    // the walks would leave at least half of the CUs idle, two workgroups per walk run the
+    // same state walk and split the output rows, so each loads the state operands and half of
+    // the output operands.
+    const int64_t walks = two ? pairs * NSTRIP / 2 : pairs * NSTRIP;
+    return rec(jobs, 1, walks * 2 <= n_cu ? 2 : 1);
   }
   // Segmented walk (sequence split of the transition form): the chunks of each sequence are
   // cut at b_1 < ... < b_{P-1}. Pass 1 walks segment 0 from S0 (its exit is segment 1's entry)
