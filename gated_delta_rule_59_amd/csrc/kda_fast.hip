@@ -85,10 +85,14 @@ __device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int3
 
 // chunk_off[n] = number of chunks of sequences 0..n-1 (lengths clamped as in seq_info), and,
 // when every > 0, ckpt_off[n] = number of state checkpoints of sequences 0..n-1 (one per full
-// `every` tokens of each).
+// `every` tokens of each). order[] lists the sequences longest first (ties by index) when
+// there are at most kMaxOrdered of them, else in their own order: the chunk walks are then
+// dispatched longest first, so the longest ones do not start last and set the tail.
+constexpr int kMaxOrdered = 512;
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int n_seq,
                                                    int T, int every, int32_t* __restrict__ chunk_off,
-                                                   int32_t* __restrict__ ckpt_off) {
+                                                   int32_t* __restrict__ ckpt_off,
+                                                   int32_t* __restrict__ order) {
   __shared__ int64_t part[2][256];
   const int t = threadIdx.x;
   const int per = (n_seq + 255) / 256;
@@ -127,6 +131,18 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
     }
   }
   if (t == 255) chunk_off[n_seq] = (int32_t)acc;
+  for (int n = lo; n < hi; ++n) {  // the rank of n is its slot: a permutation of 0..n_seq-1
+    int rank = n;
+    if (n_seq <= kMaxOrdered) {
+      const int64_t len = seq_len(n);
+      rank = 0;
+      for (int m = 0; m < n_seq; ++m) {
+        const int64_t lm = seq_len(m);
+        rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
+      }
+    }
+    order[rank] = n;
+  }
 }
 
 // ---------------------------------------------------------------- prep
@@ -812,7 +828,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
     RecJobs jobs, TOut* __restrict__ o, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_off, int T, int H, int n_seq, int64_t max_chunks,
     const uint8_t* __restrict__ ws, float* __restrict__ ckpt, int ckpt_chunks, int ckpt_slots,
-    const int32_t* __restrict__ ckpt_off) {
+    const int32_t* __restrict__ ckpt_off, const int32_t* __restrict__ order) {
   // blockIdx.x = job * blocks_per_job + (block within the job)
   // A workgroup owns NT strips of 16 value columns. One fp16 exchange per chunk through LDS,
   // followed by one barrier: the state strips entering the chunk (all 128 key rows), which the
@@ -837,7 +853,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
   const int half = r2 % jobs.halves;
   const int64_t pair = (int64_t)(r2 / jobs.halves) * 8 + xcd;
   if (pair >= (int64_t)n_seq * H) return;
-  const int n = (int)(pair / H), h = (int)(pair % H);
+  // packed sequences are walked longest first (order from the plan kernel)
+  const int n = order ? order[pair / H] : (int)(pair / H), h = (int)(pair % H);
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   // a malformed cu_seqlens cannot make the chunk walk leave the workspace
   const int64_t nc = max((int64_t)0, min((si.len + C - 1) / C, max_chunks - si.cid0));
@@ -864,7 +881,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
     // they carry the serial chain: when both roles have work ready on a SIMD, theirs issues first
     __builtin_amdgcn_s_setprio(2);
-    const int64_t s_base = pair * DK * DV;
+    const int64_t s_base = ((int64_t)n * H + h) * DK * DV;
     int col[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) col[nt] = 16 * (NT * sg + nt) + nn;
@@ -1128,7 +1145,7 @@ namespace {
 int n_segments(const ChunkPlan& p) { return p.segments >= 3 ? p.segments : 1; }
 size_t state_bytes(const ChunkPlan& p) { return (size_t)p.n_seq * p.H * DK * DV * sizeof(float); }
 size_t segment_buffers_offset(const ChunkPlan& p) {
-  return chunk_table_offset(p) + (p.cu_seqlens ? 2 * table_bytes(p) : 0);
+  return chunk_table_offset(p) + (p.cu_seqlens ? 3 * table_bytes(p) : 0);
 }
 }  // namespace
 
@@ -1142,7 +1159,7 @@ namespace {
 template <typename TOut>
 hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int halves, int64_t pairs,
                       RecJobs jobs, int n_jobs, const int32_t* chunk_off,
-                      const int32_t* ckpt_off, uint8_t* ws) {
+                      const int32_t* ckpt_off, const int32_t* order, uint8_t* ws) {
   jobs.halves = halves;
   jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP) * halves;
   const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
@@ -1150,7 +1167,7 @@ hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int halv
   auto kern = two ? rec_kernel<TOut, 2> : rec_kernel<TOut, 1>;
   hipLaunchKernelGGL(kern, grid, block, 0, stream, jobs, static_cast<TOut*>(p.o), p.cu_seqlens,
                      chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws, p.ckpt, ck_chunks,
-                     p.ckpt_slots, ckpt_off);
+                     p.ckpt_slots, ckpt_off, order);
   return hipGetLastError();
 }
 
@@ -1171,12 +1188,13 @@ hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* ch
 
 hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
-  int32_t *chunk_off = nullptr, *ckpt_off = nullptr;
+  int32_t *chunk_off = nullptr, *ckpt_off = nullptr, *order = nullptr;
   if (p.cu_seqlens) {
     chunk_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p));
     ckpt_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p) + table_bytes(p));
+    order = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p) + 2 * table_bytes(p));
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seq, p.T,
-                       p.ckpt ? p.ckpt_every : 0, chunk_off, ckpt_off);
+                       p.ckpt ? p.ckpt_every : 0, chunk_off, ckpt_off, order);
   }
   const int64_t pairs = (int64_t)p.n_seq * p.H;
   const int ncs = (int)((p.T + C - 1) / C);
@@ -1191,8 +1209,8 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
-    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws)
-                      : launch_rec<float>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, ws);
+    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, order, ws)
+                      : launch_rec<float>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, order, ws);
   };
   RecJobs jobs = {};
   const int P = n_segments(p);
