@@ -51,8 +51,8 @@ def src_hash(*paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(profile_name, kernel_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+def read_profile_value(profile_name, key, kernel_hash):
+    """A figure from a committed rocprofv3 summary under profiles/, if the summary was taken
     on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", profile_name)
     if not os.path.exists(path):
@@ -65,9 +65,14 @@ def read_traffic(profile_name, kernel_hash):
     if vals.get("kernel_src_sha") != kernel_hash:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(profile_name, kernel_hash):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE)."""
+    return read_profile_value(profile_name, "hbm_bytes_per_launch", kernel_hash)
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -281,6 +286,10 @@ def main():
     ksrc = [os.path.join(ROOT, "gated_delta_rule_59_amd", "csrc", f)
             for f in ("kda_fast.hip", "kda_device.h")]
     traffic = read_traffic(f"{args.workload}_chunk_fwd_traffic.txt", src_hash(*ksrc))
+    # executed matrix-core work (every MFMA issued, masked and repeated work included) as a
+    # fraction of the matrix peak over the launch, from the committed SQ counter summary
+    mfma_busy = read_profile_value(f"{args.workload}_sq_counters.txt", "mfma_busy_frac_launch",
+                                   src_hash(*ksrc))
     tokens = B * T
     # the roofline ceiling for this path: min(matrix peak, HBM peak x flops per byte)
     attainable = min(MFMA_PEAK_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9 * flops / nbytes)
@@ -299,6 +308,7 @@ def main():
                     "alg_tflops": tflops, "alg_mfma_frac": tflops / MFMA_PEAK_TFLOPS,
                     "alg_GB_per_s": gbs, "alg_hbm_frac": gbs / HBM_PEAK_GBS,
                     "attainable_frac": (flops / (per_ms * 1e-3)) / attainable,
+                    "rocprof_executed_mfma_busy_frac": mfma_busy,
                     "workspace_bytes": nbytes_ws,
                     "cold_event_ms_median": cold and cold[0], "cold_event_ms_min": cold and cold[1],
                     "cold_steps": args.cold_steps,
