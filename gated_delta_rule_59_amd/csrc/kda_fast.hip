@@ -32,13 +32,15 @@
 //    operands need bf16's exponent range (fp16 would overflow at e^80), and are split into
 //    bf16 hi + lo pairs (three products) to keep 16 bits of precision. Off-diagonal factors
 //    are <= 1 and use fp16 (11-bit significand) directly.
-//  rec_kernel (one workgroup per sequence, head and 16 value columns, serial over chunks):
-//    the fp32 state slice S[128][16] lives in MFMA accumulators for the whole sequence.
-//    Eight waves in two roles. Waves 0-3 own 32 key rows of the state each and carry the
-//    dependency chain: S <- S + Z + Psi S for their rows. Waves 4-7 compute the
+//  rec_kernel (one workgroup per sequence, head and strip of 16 or 32 value columns, serial
+//    over chunks): the fp32 state slice S[128][16 or 32] lives in MFMA accumulators for the
+//    whole sequence. Eight waves in two roles. Waves 0-3 own 32 key rows of the state each
+//    and carry the dependency chain: S <- S + Z + Psi S for their rows. Waves 4-7 compute the
 //    outputs Qhat S + Ohat of their 16 chunk rows from the same gathered state, off the chain.
 //    Columns of S evolve independently (the transition acts on the key side only), so
-//    splitting the value columns over workgroups is exact.
+//    splitting the value columns over workgroups is exact. When the walks would leave half of
+//    the CUs idle, two workgroups repeat each walk and split its output rows; packed
+//    sequences are walked longest first.
 #include "kda_device.h"
 #include "kda_internal.h"
 
