@@ -7,9 +7,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
+#include <cstdint>
 #include <cstring>
 #include <string>
-#include <vector>
 
 #include "kda_internal.h"
 
@@ -55,24 +56,40 @@ bool env_check() {
   return s && s[0] == '1';
 }
 
+// Counts g outside [-5, 0] and beta outside [0, 1] on the device into counts[0 .. n_counts)
+// (caller-owned device memory; at most kda::check_blocks() of them are used), copies them to
+// the host and synchronises the stream.
 kda_status run_gate_check(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
-                          kda_dtype dt, hipStream_t stream, int64_t* n_bad) {
-  const int nb = kda::check_blocks();
-  int64_t* counts = nullptr;
-  if (hipMalloc(&counts, sizeof(int64_t) * nb) != hipSuccess)
-    return fail(KDA_ERR_HIP, "kda_check_gates: hipMalloc of %d counters failed", nb);
-  hipError_t e = kda::launch_check_gates(g, n_g, beta, n_beta, dt == KDA_BF16, counts, stream);
-  std::vector<int64_t> host(nb, 0);
+                          kda_dtype dt, int64_t* counts, int64_t n_counts, hipStream_t stream,
+                          int64_t* n_bad) {
+  int64_t host[1024];
+  static_assert(sizeof(host) / sizeof(host[0]) >= 1024, "host copy of the counters");
+  const int nb = (int)std::min<int64_t>(n_counts, kda::check_blocks());
+  hipError_t e = kda::launch_check_gates(g, n_g, beta, n_beta, dt == KDA_BF16, counts, nb, stream);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(host.data(), counts, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, stream);
+    e = hipMemcpyAsync(host, counts, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  (void)hipFree(counts);
-  if (e != hipSuccess)
-    return fail(KDA_ERR_HIP, "kda_check_gates: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "gate check: %s", hipGetErrorString(e));
   int64_t total = 0;
-  for (int64_t c : host) total += c;
+  for (int i = 0; i < nb; ++i) total += host[i];
   *n_bad = total;
   return ok();
+}
+
+// KDA_CHECK=1: the gate check before a call, its counters held in the call's output buffer o
+// (which the call overwrites afterwards, and which overlaps no input), so that nothing is
+// allocated. o_bytes >= 64 (one token of one head), so at least seven 8-byte aligned
+// counters fit.
+kda_status env_gate_check(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
+                          kda_dtype dt, void* o, size_t o_bytes, hipStream_t stream) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(o), end = lo + o_bytes;
+  const uintptr_t c0 = (lo + 7) & ~uintptr_t(7);
+  int64_t bad = 0;
+  kda_status s = run_gate_check(g, n_g, beta, n_beta, dt, reinterpret_cast<int64_t*>(c0),
+                                (int64_t)((end - c0) / sizeof(int64_t)), stream, &bad);
+  if (s != KDA_OK) return s;
+  if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
+  return KDA_OK;
 }
 
 // Shape/dtype validation shared by kda_chunk_fwd and kda_chunk_fwd_workspace.
@@ -126,13 +143,11 @@ bool use_fast(const kda_chunk_args* a, const kda::ChunkPlan& p) {
 
 extern "C" {
 
-kda_status kda_chunk_fwd_workspace(const kda_chunk_args* a, size_t* bytes) {
-  if (!bytes) return fail(KDA_ERR_NULL_PTR, "bytes is NULL");
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* a) {
   kda::ChunkPlan p;
-  kda_status s = validate_chunk_shapes(a, &p);
-  if (s != KDA_OK) return s;
-  *bytes = use_fast(a, p) ? kda::fast_workspace_bytes(p) : 0;
-  return ok();
+  if (validate_chunk_shapes(a, &p) != KDA_OK) return SIZE_MAX;
+  ok();
+  return use_fast(a, p) ? kda::fast_workspace_bytes(p) : 0;
 }
 
 kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
@@ -182,12 +197,10 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
       return fail(KDA_ERR_ALIAS, "workspace overlaps an output");
   }
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (env_check()) {
-    int64_t bad = 0;
-    s = run_gate_check(a->g, (int64_t)(tok * a->dk), a->beta, (int64_t)tok, a->gate_dtype, stream,
-                       &bad);
+  if (env_check() && tok > 0) {
+    s = env_gate_check(a->g, (int64_t)(tok * a->dk), a->beta, (int64_t)tok, a->gate_dtype, a->o,
+                       tok * a->dv * os, stream);
     if (s != KDA_OK) return s;
-    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
   }
   const hipError_t e = fast ? kda::launch_chunk_fast(p, stream) : kda::launch_chunk_generic(p, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
@@ -221,11 +234,9 @@ kda_status kda_decode_step(const kda_decode_args* a, void* hip_stream) {
   if (overlap(S, o)) return fail(KDA_ERR_ALIAS, "S overlaps o");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (env_check()) {
-    int64_t bad = 0;
-    kda_status s = run_gate_check(a->g, (int64_t)(nh * a->dk), a->beta, (int64_t)nh,
-                                  a->gate_dtype, stream, &bad);
+    kda_status s = env_gate_check(a->g, (int64_t)(nh * a->dk), a->beta, (int64_t)nh,
+                                  a->gate_dtype, a->o, nh * a->dv * os, stream);
     if (s != KDA_OK) return s;
-    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
   }
   const kda::DecodePlan p{a->N, a->H, a->dk, a->dv, a->act_dtype == KDA_BF16,
                           a->out_dtype == KDA_BF16, a->q, a->k, a->v, a->g, a->beta, a->S, a->o};
@@ -264,11 +275,11 @@ kda_status kda_decode_multi(const kda_decode_multi_args* a, void* hip_stream) {
   if (!a->o && !a->accept) return ok();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (env_check()) {
-    int64_t bad = 0;
-    kda_status s = run_gate_check(a->g, (int64_t)(nmh * a->dk), a->beta, (int64_t)nmh,
-                                  a->gate_dtype, stream, &bad);
+    if (!a->o)
+      return fail(KDA_ERR_UNSUPPORTED, "KDA_CHECK=1 needs o (the check keeps its counters there)");
+    kda_status s = env_gate_check(a->g, (int64_t)(nmh * a->dk), a->beta, (int64_t)nmh,
+                                  a->gate_dtype, a->o, nmh * a->dv * os, stream);
     if (s != KDA_OK) return s;
-    if (bad) return fail(KDA_ERR_DECAY_RANGE, "%lld gate values outside their range", (long long)bad);
   }
   const kda::DecodeMultiPlan p{a->N, a->H, a->dk, a->dv, a->m, a->act_dtype == KDA_BF16,
                                a->out_dtype == KDA_BF16, a->q, a->k, a->v, a->g, a->beta,
@@ -279,13 +290,21 @@ kda_status kda_decode_multi(const kda_decode_multi_args* a, void* hip_stream) {
 }
 
 kda_status kda_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
-                           kda_dtype gate_dtype, void* hip_stream, int64_t* n_bad) {
+                           kda_dtype gate_dtype, int64_t* counts, int n_counts,
+                           void* hip_stream, int64_t* n_bad) {
   if (!n_bad) return fail(KDA_ERR_NULL_PTR, "n_bad is NULL");
   if (n_g < 0 || n_beta < 0) return fail(KDA_ERR_BAD_SHAPE, "negative element count");
   if ((n_g && !g) || (n_beta && !beta)) return fail(KDA_ERR_NULL_PTR, "g or beta is NULL");
+  if (!counts) return fail(KDA_ERR_NULL_PTR, "counts is NULL");
+  if (n_counts < 1) return fail(KDA_ERR_BAD_SHAPE, "n_counts must be >= 1 (got %d)", n_counts);
   if (!dtype_ok(gate_dtype)) return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
-  return run_gate_check(g, n_g, beta, n_beta, gate_dtype, static_cast<hipStream_t>(hip_stream),
-                        n_bad);
+  const size_t es = dsize(gate_dtype);
+  const size_t used = sizeof(int64_t) * (size_t)std::min(n_counts, kda::check_blocks());
+  const Range c = range("counts", counts, used);
+  if (overlap(c, range("g", g, (size_t)n_g * es)) || overlap(c, range("beta", beta, (size_t)n_beta * es)))
+    return fail(KDA_ERR_ALIAS, "counts overlaps g or beta");
+  return run_gate_check(g, n_g, beta, n_beta, gate_dtype, counts, n_counts,
+                        static_cast<hipStream_t>(hip_stream), n_bad);
 }
 
 const char* kda_status_string(kda_status s) {

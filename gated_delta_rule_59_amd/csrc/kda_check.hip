@@ -2,6 +2,8 @@
 // per-step log-decay from the orkas.ai Kimi K3 page, section "Eine Untergrenze, die einen
 // GPU-Codepfad beseitigte") and every beta in [0, 1]. NaN counts as a violation.
 // Each block writes its own count (no atomics); the host adds them up.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -39,13 +41,14 @@ __global__ __launch_bounds__(256) void check_gates_kernel(const T* __restrict__ 
 int check_blocks() { return kCheckBlocks; }
 
 hipError_t launch_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
-                              bool bf16, int64_t* counts, hipStream_t stream) {
+                              bool bf16, int64_t* counts, int n_blocks, hipStream_t stream) {
+  const dim3 grid((unsigned)std::min(std::max(n_blocks, 1), kCheckBlocks));
   if (bf16)
-    hipLaunchKernelGGL(check_gates_kernel<uint16_t>, dim3(kCheckBlocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(check_gates_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(g), n_g, static_cast<const uint16_t*>(beta),
                        n_beta, counts);
   else
-    hipLaunchKernelGGL(check_gates_kernel<float>, dim3(kCheckBlocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(check_gates_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const float*>(g), n_g, static_cast<const float*>(beta), n_beta,
                        counts);
   return hipGetLastError();

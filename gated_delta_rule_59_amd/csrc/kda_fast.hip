@@ -43,6 +43,7 @@
 //    sequences are walked longest first.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_plan.h"
 
 namespace kda {
 
@@ -875,7 +876,9 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
   const int64_t ck_base =
       ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
-  // the second workgroup of a split pair repeats the walk: only the first writes states
+  // the second workgroup of a split pair repeats the walk: only the first writes states. Both
+  // read S0 when they start, so the split assumes S0 is not written during the launch (the
+  // host never splits an in-place walk, where S_T is the S0 buffer).
   const int ck_every = job.mode == REC_OUTPUT && half == 0 ? ckpt_chunks : 0;
   if (half != 0) S_T = nullptr;
 
@@ -1207,7 +1210,8 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   // workgroup maximises parallelism. At least one strip per CU: two strips per workgroup halve
   // the state operand traffic per column (the walk is bound by each CU's vector memory unit);
   // measured faster from one strip per CU on (prefill-64k-bound -1.5 %).
-  const bool two = pairs * NSTRIP >= (int64_t)n_cu;
+  const WalkShape shape = walk_shape(pairs, n_cu, p.S0 != nullptr && p.S0 == p.S_T);
+  const bool two = shape.two_strips;
   hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
@@ -1221,9 +1225,8 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     // The walk is bound by each CU's vector memory unit (the operand bytes per chunk). When
     // the walks would leave at least half of the CUs idle, two workgroups per walk run the
     // same state walk and split the output rows, so each loads the state operands and half of
-    // the output operands.
-    const int64_t walks = two ? pairs * NSTRIP / 2 : pairs * NSTRIP;
-    return rec(jobs, 1, walks * 2 <= n_cu ? 2 : 1);
+    // the output operands (never in place: see walk_shape).
+    return rec(jobs, 1, shape.halves);
   }
   // Segmented walk (sequence split of the transition form): the chunks of each sequence are
   // cut at b_1 < ... < b_{P-1}. Pass 1 walks segment 0 from S0 (its exit is segment 1's entry)

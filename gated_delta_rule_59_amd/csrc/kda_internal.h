@@ -56,10 +56,10 @@ bool fast_path_applies(const ChunkPlan& p);
 size_t fast_workspace_bytes(const ChunkPlan& p);
 hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream);
 
-// Device check of g in [-5, 0] and beta in [0, 1]; writes per-block counts of violations
-// into counts[0 .. n_blocks) (n_blocks = check_blocks()).
+// Device check of g in [-5, 0] and beta in [0, 1] over n_blocks workgroups (1 .. check_blocks());
+// writes each workgroup's count of violations into counts[0 .. n_blocks).
 int check_blocks();
 hipError_t launch_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
-                              bool bf16, int64_t* counts, hipStream_t stream);
+                              bool bf16, int64_t* counts, int n_blocks, hipStream_t stream);
 
 }  // namespace kda

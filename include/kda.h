@@ -34,9 +34,14 @@
  *     returns without synchronising. Launch failures are reported as KDA_ERR_HIP.
  *   - Nothing is printed and no exception crosses the ABI.
  *   - Preconditions not checked by default: g in [-5, 0], beta in [0, 1], q and k rows of
- *     unit L2 norm. With the environment variable KDA_CHECK=1, kda_chunk_fwd and
- *     kda_decode_step first run a device check of g and beta, synchronise the stream and
- *     return KDA_ERR_DECAY_RANGE if any value is outside its range. Nothing is clamped.
+ *     unit L2 norm. With the environment variable KDA_CHECK=1, kda_chunk_fwd, kda_decode_step
+ *     and kda_decode_multi first run a device check of g and beta, synchronise the stream and
+ *     return KDA_ERR_DECAY_RANGE if any value is outside its range. The check keeps its
+ *     counters in the call's output buffer o (overwritten by the call afterwards; o overlaps
+ *     no input), so it allocates nothing; kda_decode_multi without o then returns
+ *     KDA_ERR_UNSUPPORTED. Nothing is clamped.
+ *   - When a call returns an error after enqueueing work (KDA_ERR_HIP, KDA_ERR_DECAY_RANGE),
+ *     the contents of its outputs are unspecified.
  *   - Layout: token-major, [B, T, H, d] contiguous (d fastest). States [n_seq, H, dk, dv]
  *     fp32 row-major (key channel rows, value channel columns).
  */
@@ -50,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -59,7 +64,7 @@ typedef enum {
     KDA_ERR_BAD_DTYPE = 3,    /* dtype combination not offered */
     KDA_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement */
     KDA_ERR_DECAY_RANGE = 5,  /* KDA_CHECK=1 found g outside [-5, 0] or beta outside [0, 1] */
-    KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than kda_chunk_fwd_workspace() */
+    KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than kda_chunk_fwd_workspace_bytes() */
     KDA_ERR_HIP = 7,          /* a HIP runtime call or kernel launch failed */
     KDA_ERR_ALIAS = 8         /* an output overlaps an input it must not overlap */
 } kda_status;
@@ -88,7 +93,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   o          [B, T, H, dv] out_dtype. Written. Must not overlap any input.
  *   S_T        [n_seq, H, dk, dv] fp32 final states, or NULL. May be the same buffer as S0
  *              (continue in place); must not partially overlap it.
- *   workspace  device scratch of at least kda_chunk_fwd_workspace() bytes (may be NULL
+ *   workspace  device scratch of at least kda_chunk_fwd_workspace_bytes() bytes (may be NULL
  *              when that is 0), 256-byte aligned; contents on entry are ignored.
  *   flags      0, or any of:
  *              KDA_FLAG_GENERIC to force the fp32 vector-ALU path (needs no workspace; slower;
@@ -183,9 +188,10 @@ typedef struct {
 } kda_decode_multi_args;
 
 /* Bytes of device workspace kda_chunk_fwd needs for these arguments (pointers are not
- * inspected). Writes 0 to *bytes when the chosen path needs none. Validates shapes and
- * dtypes like kda_chunk_fwd. */
-kda_status kda_chunk_fwd_workspace(const kda_chunk_args* args, size_t* bytes);
+ * inspected); 0 when the chosen path needs none. Validates shapes and dtypes like
+ * kda_chunk_fwd and returns SIZE_MAX (with kda_last_error() set) when they are invalid.
+ * The matrix-core path needs one 114,688-byte block per (chunk, head) plus small tables. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* args);
 
 /* Prefill: o and S_T from q, k, v, g, beta and S0, enqueued on hip_stream (hipStream_t). */
 kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
@@ -198,10 +204,18 @@ kda_status kda_decode_step(const kda_decode_args* args, void* hip_stream);
 kda_status kda_decode_multi(const kda_decode_multi_args* args, void* hip_stream);
 
 /* Device check of the preconditions on the gates: counts g values outside [-5, 0] and
- * beta values outside [0, 1] (NaN counts as outside). n_g, n_beta elements; dtype of both
- * is gate_dtype. Synchronises hip_stream; *n_bad receives the count. */
+ * beta values outside [0, 1] (NaN counts as outside); the floor of -5 is the bound on the
+ * per-step log-decay (orkas.ai Kimi K3 page, "Eine Untergrenze, die einen GPU-Codepfad
+ * beseitigte"). n_g, n_beta elements; dtype of both is gate_dtype.
+ *   counts    caller-owned device scratch of n_counts int64 (n_counts >= 1; up to
+ *             KDA_CHECK_COUNTERS of them are used, one per workgroup of the check, so
+ *             KDA_CHECK_COUNTERS entries give the most parallel check). Must not overlap g or
+ *             beta; its contents on return are unspecified.
+ * Synchronises hip_stream; *n_bad receives the count. Allocates nothing. */
+#define KDA_CHECK_COUNTERS 1024
 kda_status kda_check_gates(const void* g, int64_t n_g, const void* beta, int64_t n_beta,
-                           kda_dtype gate_dtype, void* hip_stream, int64_t* n_bad);
+                           kda_dtype gate_dtype, int64_t* counts, int n_counts,
+                           void* hip_stream, int64_t* n_bad);
 
 const char* kda_status_string(kda_status s);
 const char* kda_last_error(void);   /* detail of the last failure on this thread */

@@ -44,11 +44,16 @@ int main(void) {
 
   /* workspace: the matrix-core path needs one 114,688-byte block per (chunk, head) */
   kda_chunk_args a = base_args();
-  size_t bytes = 0;
-  EXPECT(kda_chunk_fwd_workspace(&a, &bytes) == KDA_OK, "workspace query: %s", kda_last_error());
+  size_t bytes = kda_chunk_fwd_workspace_bytes(&a);
+  EXPECT(bytes != SIZE_MAX, "workspace query: %s", kda_last_error());
   EXPECT(bytes >= (size_t)4 * 4 * 114688, "workspace %zu bytes", bytes);
   a.flags = KDA_FLAG_GENERIC;
-  EXPECT(kda_chunk_fwd_workspace(&a, &bytes) == KDA_OK && bytes == 0, "fp32 path workspace %zu", bytes);
+  bytes = kda_chunk_fwd_workspace_bytes(&a);
+  EXPECT(bytes == 0, "fp32 path workspace %zu", bytes);
+  a = base_args();
+  a.dk = 96;
+  EXPECT(kda_chunk_fwd_workspace_bytes(&a) == SIZE_MAX && strlen(kda_last_error()) > 0,
+         "workspace query of a bad shape");
 
   /* validation before any launch */
   a = base_args();
@@ -75,8 +80,16 @@ int main(void) {
   EXPECT(kda_decode_multi(&m, NULL) == KDA_ERR_BAD_SHAPE, "decode_multi m=0");
 
   int64_t n_bad = -1;
-  EXPECT(kda_check_gates(NULL, 10, NULL, 0, KDA_BF16, NULL, &n_bad) == KDA_ERR_NULL_PTR,
+  EXPECT(kda_check_gates(NULL, 10, NULL, 0, KDA_BF16, NULL, KDA_CHECK_COUNTERS, NULL, &n_bad) ==
+             KDA_ERR_NULL_PTR,
          "check_gates NULL g");
+  EXPECT(kda_check_gates((const void*)((uintptr_t)1 << 40), 10, NULL, 0, KDA_BF16, NULL,
+                         KDA_CHECK_COUNTERS, NULL, &n_bad) == KDA_ERR_NULL_PTR,
+         "check_gates NULL counts");
+  EXPECT(kda_check_gates((const void*)((uintptr_t)1 << 40), 10, NULL, 0, KDA_BF16,
+                         (int64_t*)((uintptr_t)1 << 40), KDA_CHECK_COUNTERS, NULL, &n_bad) ==
+             KDA_ERR_ALIAS,
+         "check_gates counts on g");
 
   if (failures == 0) printf("ok\n");
   return failures ? 1 : 0;

@@ -9,13 +9,22 @@ def rms(x):
     return float(np.sqrt(np.mean(np.square(np.asarray(x, np.float64)))))
 
 
-def max_rel_err(got, ref):
-    """max |got - ref| / RMS(ref) over the whole tensor."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
+def max_rel_err(got, ref, block=1 << 24):
+    """max |got - ref| / RMS(ref) over the whole tensor, in blocks of `block` elements (the
+    full-size workloads hold hundreds of millions of values)."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    assert np.isfinite(got).all(), "non-finite values in GPU result"
-    return float(np.abs(got - ref).max() / rms(ref))
+    g = got.reshape(-1)
+    r = ref.reshape(-1)
+    worst, sq = 0.0, 0.0
+    for a in range(0, g.size, block):
+        gb = g[a:a + block].astype(np.float64)
+        rb = r[a:a + block].astype(np.float64)
+        assert np.isfinite(gb).all(), "non-finite values in GPU result"
+        worst = max(worst, float(np.abs(gb - rb).max()))
+        sq += float(np.dot(rb, rb))
+    return worst / float(np.sqrt(sq / max(g.size, 1)))
 
 
 def assert_parity(got, ref, tau, what):

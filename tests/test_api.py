@@ -28,12 +28,12 @@ def declared_functions():
 
 def test_exports_every_declared_function(b):
     names = declared_functions()
-    assert set(names) >= {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace",
+    assert set(names) >= {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
                           "kda_check_gates", "kda_status_string", "kda_last_error",
                           "kda_abi_version"}
     for n in names:
         assert hasattr(b.lib(), n), n
-    assert b.lib().kda_abi_version() == b.ABI_VERSION == 3
+    assert b.lib().kda_abi_version() == b.ABI_VERSION == 4
 
 
 def test_status_strings(b):
@@ -112,19 +112,16 @@ def test_chunk_checkpoint_rules(b):
 
 
 def test_workspace_query(b):
-    n = ctypes.c_size_t(123)
-    a = base_args(b)
-    assert b.lib().kda_chunk_fwd_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
-    fast = n.value
-    a = base_args(b, flags=b.KDA_FLAG_GENERIC)
-    assert b.lib().kda_chunk_fwd_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
-    assert n.value == 0
-    a = base_args(b, act_dtype=b.KDA_F32, gate_dtype=b.KDA_F32)
-    assert b.lib().kda_chunk_fwd_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
-    assert n.value == 0
-    assert b.lib().kda_chunk_fwd_workspace(ctypes.byref(a), None) == 1
-    if fast:   # the matrix-core path needs scratch and refuses to run without it
-        assert call_chunk(b, base_args(b))[0] == 6
+    q = lambda a: b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a))  # noqa: E731
+    fast = q(base_args(b))
+    # one 114,688-byte block per (chunk, head): 4 chunks of 64 tokens, 4 heads
+    assert fast >= 4 * 4 * 114688
+    assert q(base_args(b, flags=b.KDA_FLAG_GENERIC)) == 0
+    assert q(base_args(b, act_dtype=b.KDA_F32, gate_dtype=b.KDA_F32)) == 0
+    assert q(base_args(b, dk=96)) == b.SIZE_MAX and b.lib().kda_last_error()
+    assert b.lib().kda_chunk_fwd_workspace_bytes(None) == b.SIZE_MAX
+    # the matrix-core path needs scratch and refuses to run without it
+    assert call_chunk(b, base_args(b))[0] == 6
 
 
 def test_decode_rejects_bad_args(b):
@@ -175,9 +172,14 @@ def test_decode_multi_rejects_bad_args(b):
 
 def test_check_gates_rejects_bad_args(b):
     n = ctypes.c_int64(0)
-    assert b.lib().kda_check_gates(None, 10, None, 0, 1, None, ctypes.byref(n)) == 1
-    assert b.lib().kda_check_gates(None, -1, None, 0, 1, None, ctypes.byref(n)) == 2
-    assert b.lib().kda_check_gates(None, 0, None, 0, 1, None, None) == 1
+    cnt = FAKE + (1 << 34)
+    call = b.lib().kda_check_gates
+    assert call(None, 10, None, 0, 1, cnt, 1024, None, ctypes.byref(n)) == 1
+    assert call(None, -1, None, 0, 1, cnt, 1024, None, ctypes.byref(n)) == 2
+    assert call(None, 0, None, 0, 1, cnt, 1024, None, None) == 1
+    assert call(FAKE, 10, None, 0, 1, None, 1024, None, ctypes.byref(n)) == 1   # no counters
+    assert call(FAKE, 10, None, 0, 1, cnt, 0, None, ctypes.byref(n)) == 2       # no room
+    assert call(FAKE, 10, None, 0, 1, FAKE + 8, 1024, None, ctypes.byref(n)) == 8  # on g
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -15,8 +15,12 @@ def test_algorithmic_counts():
     # 5 C d + 6 d^2 at C = 64, d = 128: A and Aqk, the solve for both right-hand sides,
     # Aqk U', and the three state products
     assert bench.flops_per_token_head() == 5 * 64 * 128 + 6 * 128 * 128 == 139264
-    # q, k, g, v and beta in bf16, o in fp32
-    assert bench.bytes_per_token_head() == 4 * 128 * 2 + 2 + 128 * 4 == 1538
+    # minimal bytes: q, k, g, v and beta in bf16 read once, a bf16-sized o written once
+    assert bench.bytes_per_token_head() == 4 * 128 * 2 + 2 + 128 * 2 == 1282
+    # the same with the fp32 o this build writes
+    assert bench.bytes_per_token_head(out_bytes=4) == 1538
+    # S0 read and S_T written once, fp32: 128 KiB per (sequence, head)
+    assert bench.state_bytes(1, 16) == 16 * 2 * 4 * 128 * 128
 
 
 def test_traffic_needs_matching_sources(tmp_path, monkeypatch):

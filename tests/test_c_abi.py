@@ -26,3 +26,20 @@ def test_c_client_links_and_validates(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith("ok")
+
+
+def test_walk_shape_never_splits_an_in_place_walk(tmp_path):
+    """The matrix-core walk's launch shape (kda_plan.h), checked on the host: two workgroups
+    per walk only when the walks leave half of the CUs idle, and never when S_T is the S0
+    buffer (the second workgroup reads S0 when it starts, possibly after the first stored
+    S_T)."""
+    if shutil.which("g++") is None:
+        pytest.skip("no g++")
+    exe = tmp_path / "plan_check"
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "gated_delta_rule_59_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "c", "plan_check.cpp"), "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip() == "ok"

@@ -53,37 +53,51 @@ def _sampled(arrs, chains):
     return [np.ascontiguousarray(np.stack([a[n, h] for n, h in chains])[:, None]) for a in arrs]
 
 
-def test_decode_workload_1000_steps_sampled():
+def test_decode_workload_1000_steps():
     """The decode workload at full size: N=512, H=32, dk=dv=128, fp32 state of 1 GiB updated
-    in place for 1000 steps. o is checked at steps 1-10, 100 and 1000 and the state at step
-    1000, on 64 sampled (sequence, head) chains that the oracle follows step by step."""
+    in place for 1000 steps.
+    Steps 1-10: o of every one of the 16,384 (sequence, head) chains against the fp64 oracle,
+    which follows all of them, and the whole state after step 10.
+    Steps 11-1000: 256 sampled chains (the first and the last included) continue in the
+    oracle; their o is checked at steps 100 and 1000 and their state at step 1000."""
     import torch
     from gated_delta_rule_59_amd import binding
     N, H, dk, dv, steps = 512, 32, 128, 128, 1000
-    print("decode workload: generating state and step inputs", flush=True)
+    threads = oracle.threads_used()
+    print(f"decode workload: generating state and step inputs (oracle on {threads} threads)",
+          flush=True)
     S_host = inputs.make_decode_state(N, H, dk, dv)
     pool = [inputs.make_decode_step(p, N, H, dk, dv) for p in range(inputs.DECODE_POOL)]
     pool_dev = [[dev(a, "bf16") for a in step] for step in pool]
-    rng = np.random.default_rng(123)
-    chains = sorted({(int(a), int(b)) for a, b in zip(rng.integers(0, N, 64), rng.integers(0, H, 64))})
-    chains[:2] = [(0, 0), (N - 1, H - 1)]
-    s_ref = np.stack([S_host[n, h] for n, h in chains])[:, None].astype(np.float64)
     S = torch.from_numpy(S_host).cuda()
+    s_all = S_host.astype(np.float64)
     del S_host
     o = torch.empty((N, H, dv), dtype=torch.float32, device="cuda")
-    check = set(range(1, 11)) | {100, 1000}
-    for s in range(1, steps + 1):
+    for s in range(1, 11):
+        p = (s - 1) % inputs.DECODE_POOL
+        binding.decode_step(*pool_dev[p], S, o=o)
+        o_ref, s_all = oracle.kda_decode_reference(*pool[p], s_all, threads=threads)
+        torch.cuda.synchronize()
+        assert_parity(o.cpu().numpy(), o_ref, TAU["bf16"], f"o step {s} (all 16384 chains)")
+    assert_parity(S.cpu().numpy(), s_all, TAU["bf16"], "S after step 10 (all 16384 chains)")
+
+    rng = np.random.default_rng(123)
+    chains = sorted({(int(a), int(b)) for a, b in zip(rng.integers(0, N, 256), rng.integers(0, H, 256))})
+    chains[:2] = [(0, 0), (N - 1, H - 1)]
+    s_ref = np.stack([s_all[n, h] for n, h in chains])[:, None]
+    del s_all
+    for s in range(11, steps + 1):
         p = (s - 1) % inputs.DECODE_POOL
         binding.decode_step(*pool_dev[p], S, o=o)
         q, k, v, g, beta = _sampled(pool[p], chains)
         o_ref, s_ref = oracle.kda_decode_reference(q, k, v, g, beta, s_ref)
-        if s in check:
+        if s in (100, 1000):
             torch.cuda.synchronize()
             oh = o.cpu().numpy()
             got = np.stack([oh[n, h] for n, h in chains])[:, None]
-            assert_parity(got, o_ref, TAU["bf16"], f"o step {s}")
+            assert_parity(got, o_ref, TAU["bf16"], f"o step {s} ({len(chains)} chains)")
     torch.cuda.synchronize()
     idx_n = torch.tensor([n for n, _ in chains], device="cuda")
     idx_h = torch.tensor([h for _, h in chains], device="cuda")
     got_s = S[idx_n, idx_h].cpu().numpy()[:, None]
-    assert_parity(got_s, s_ref, TAU["bf16"], "S step 1000")
+    assert_parity(got_s, s_ref, TAU["bf16"], f"S step 1000 ({len(chains)} chains)")
