@@ -24,6 +24,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ER
 _P = ctypes.c_void_p
 SIZE_MAX = ctypes.c_size_t(-1).value
 CHECK_COUNTERS = 1024  # KDA_CHECK_COUNTERS
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class ChunkArgs(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkArgs), _P]
         L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkArgs), _P]
+        L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_multi.argtypes = [ctypes.POINTER(DecodeMultiArgs), _P]
@@ -220,6 +223,23 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
                    workspace=workspace, generic=generic, ckpt=ckpt if ckpt_every else None,
                    ckpt_every=ckpt_every, pairwise_diag=pairwise_diag, segments=segments)
     _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, S0=None, cu_seqlens=None, *, o, S_T=None, chunk=64,
+                      generic=False, stream=None, ckpt=None, ckpt_every=0, segments=0):
+    """kda_chunk_fwd_noalloc: the prefill with the library's fixed device scratch in place of
+    a workspace; o (and S_T, ckpt when wanted) are the caller's, nothing is allocated here.
+    Raises KDAError (KDA_ERR_WORKSPACE) when the sizes need more than NOALLOC_SCRATCH_BYTES."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o)):
+        _dev(t, name)
+    for name, t in (("S0", S0), ("S_T", S_T), ("cu_seqlens", cu_seqlens), ("ckpt", ckpt)):
+        if t is not None:
+            _dev(t, name)
+    a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
+                   generic=generic, ckpt=ckpt if ckpt_every else None, ckpt_every=ckpt_every,
+                   segments=segments)
+    _check(lib().kda_chunk_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return o, S_T
 
 

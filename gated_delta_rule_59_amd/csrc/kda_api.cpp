@@ -139,18 +139,9 @@ bool use_fast(const kda_chunk_args* a, const kda::ChunkPlan& p) {
   return !(a->flags & KDA_FLAG_GENERIC) && kda::fast_path_applies(p);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* a) {
-  kda::ChunkPlan p;
-  if (validate_chunk_shapes(a, &p) != KDA_OK) return SIZE_MAX;
-  ok();
-  return use_fast(a, p) ? kda::fast_workspace_bytes(p) : 0;
-}
-
-kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
+// kda_chunk_fwd and kda_chunk_fwd_noalloc. With noalloc the workspace fields of *a are
+// ignored and the library's fixed device scratch takes the workspace's place.
+kda_status chunk_fwd(const kda_chunk_args* a, void* hip_stream, bool noalloc) {
   kda::ChunkPlan p;
   kda_status s = validate_chunk_shapes(a, &p);
   if (s != KDA_OK) return s;
@@ -183,7 +174,20 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
   if (overlap(ck, o) || overlap(ck, sT)) return fail(KDA_ERR_ALIAS, "ckpt overlaps an output");
 
   const bool fast = use_fast(a, p);
-  if (fast) {
+  if (fast && noalloc) {
+    const size_t need = kda::fast_workspace_bytes(p);
+    if (need > kda::noalloc_scratch_bytes())
+      return fail(KDA_ERR_WORKSPACE,
+                  "kda_chunk_fwd_noalloc: these sizes need %zu bytes of scratch, more than the "
+                  "%zu bytes of the library's fixed scratch (use kda_chunk_fwd with a workspace)",
+                  need, kda::noalloc_scratch_bytes());
+    void* ws = nullptr;
+    const hipError_t e = kda::noalloc_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(KDA_ERR_HIP, "kda_chunk_fwd_noalloc: scratch address: %s", hipGetErrorString(e));
+    p.workspace = ws;
+    p.workspace_bytes = kda::noalloc_scratch_bytes();
+  } else if (fast) {
     const size_t need = kda::fast_workspace_bytes(p);
     if (need && (!a->workspace || a->workspace_bytes < need))
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -205,6 +209,25 @@ kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
   const hipError_t e = fast ? kda::launch_chunk_fast(p, stream) : kda::launch_chunk_generic(p, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const kda_chunk_args* a, void* hip_stream) {
+  return chunk_fwd(a, hip_stream, false);
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_args* a, void* hip_stream) {
+  return chunk_fwd(a, hip_stream, true);
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* a) {
+  kda::ChunkPlan p;
+  if (validate_chunk_shapes(a, &p) != KDA_OK) return SIZE_MAX;
+  ok();
+  return use_fast(a, p) ? kda::fast_workspace_bytes(p) : 0;
 }
 
 kda_status kda_decode_step(const kda_decode_args* a, void* hip_stream) {

@@ -56,6 +56,11 @@ bool fast_path_applies(const ChunkPlan& p);
 size_t fast_workspace_bytes(const ChunkPlan& p);
 hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream);
 
+// Fixed device scratch of the allocation-free prefill entry point: its size, and its device
+// address on the current device (looked up on the first call per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 // Device check of g in [-5, 0] and beta in [0, 1] over n_blocks workgroups (1 .. check_blocks());
 // writes each workgroup's count of violations into counts[0 .. n_blocks).
 int check_blocks();

@@ -196,6 +196,19 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* args);
 /* Prefill: o and S_T from q, k, v, g, beta and S0, enqueued on hip_stream (hipStream_t). */
 kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
 
+/* Prefill without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments
+ * and results as kda_chunk_fwd, except that workspace and workspace_bytes are ignored: the
+ * library's own fixed device scratch of KDA_NOALLOC_SCRATCH_BYTES takes the workspace's place.
+ * That scratch is a static array of the library, held by every GPU the library runs on from
+ * the first use there until the process ends. Calls whose kda_chunk_fwd_workspace_bytes()
+ * exceeds KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything is enqueued (at
+ * most 1,170 (chunk, head) pairs of 64 tokens, e.g. 4,096 tokens with 16 heads). No device
+ * or host memory is allocated. All calls on one GPU share its scratch, whatever their stream:
+ * calls that overlap in time on one GPU race (serialise them, e.g. on one stream). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_args* args, void* hip_stream);
+
 /* Decode: one step for every (sequence, head); S updated in place, o written. */
 kda_status kda_decode_step(const kda_decode_args* args, void* hip_stream);
 

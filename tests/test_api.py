@@ -124,6 +124,19 @@ def test_workspace_query(b):
     assert call_chunk(b, base_args(b))[0] == 6
 
 
+def test_noalloc_refuses_sizes_beyond_its_scratch(b):
+    """kda_chunk_fwd_noalloc checks its sizes against the fixed scratch before touching a
+    device: 1,171 (chunk, head) blocks of 114,688 B exceed KDA_NOALLOC_SCRATCH_BYTES."""
+    assert b.NOALLOC_SCRATCH_BYTES == 128 << 20
+    a = base_args(b, T=64 * 1171, H=1)
+    tok = 64 * 1171
+    a.k, a.v, a.g, a.beta = (FAKE + i * tok * 128 * 2 for i in range(1, 5))
+    a.o = FAKE + (1 << 34)
+    rc = b.lib().kda_chunk_fwd_noalloc(ctypes.byref(a), None)
+    assert rc == 6 and "scratch" in b.lib().kda_last_error().decode()
+    assert b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a)) > b.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_rejects_bad_args(b):
     a = b.DecodeArgs()
     a.N, a.H, a.dk, a.dv = 4, 2, 128, 128

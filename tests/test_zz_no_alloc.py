@@ -1,0 +1,71 @@
+"""kda_chunk_fwd_noalloc (the prefill with the library's fixed device scratch instead of a
+caller workspace) against kda_chunk_fwd on the GPU, through the C ABI: two calls in a row,
+the second with a smaller input, each bitwise equal to kda_chunk_fwd on the same inputs
+(the same kernels run on the same values), and within the bf16 bar of the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_59_amd import inputs
+from tests.gpu_util import TAU, assert_parity, host, kda_inputs_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(x, **kw):
+    import torch
+    from gated_delta_rule_59_amd import binding
+    q, k, v, g, beta, S0, cu = kda_inputs_dev(x)
+    o_ref, s_ref = binding.chunk_fwd(q, k, v, g, beta, S0, cu, **kw)
+    o = torch.full_like(o_ref, float("nan"))
+    s = torch.full_like(s_ref, float("nan"))
+    binding.chunk_fwd_noalloc(q, k, v, g, beta, S0, cu, o=o, S_T=s, **kw)
+    torch.cuda.synchronize()
+    return o, s, o_ref, s_ref
+
+
+def test_noalloc_matches_chunk_fwd_twice_then_smaller():
+    import torch
+    cases = [("prefill-4k full size (1,024 chunk-head blocks, 117 MB of scratch)",
+              inputs.make_prefill(1), {}),
+             ("T=300 H=2, a smaller input after a larger one", inputs.make_prefill(1, T=300, H=2), {})]
+    for label, x, kw in cases:
+        print(f"noalloc: {label}", flush=True)
+        o, s, o_ref, s_ref = _both(x, **kw)
+        assert torch.equal(o, o_ref) and torch.equal(s, s_ref), label
+        if x.wl.T <= 400:
+            ro, rs = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0)
+            assert_parity(host(o), ro, TAU["bf16"], f"{label} o")
+            assert_parity(host(s), rs, TAU["bf16"], f"{label} S_T")
+
+
+def test_noalloc_varlen_and_segments():
+    """The packed path (its tables live in the scratch) and the segmented walk (its entry
+    states, summaries and transitions live there too) after other calls have left their
+    contents in the scratch."""
+    import torch
+    from tests.test_gpu_generic import ragged_case
+    print("noalloc: ragged varlen", flush=True)
+    o, s, o_ref, s_ref = _both(ragged_case(H=4))
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+    print("noalloc: 3 segments, B=1 T=2048 H=2", flush=True)
+    x = inputs.make_prefill(2, T=2048, H=2)
+    o, s, o_ref, s_ref = _both(x, segments=3)
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+
+
+def test_noalloc_rejects_more_than_its_scratch():
+    """Sizes whose workspace exceeds the fixed scratch are refused before any launch, with the
+    output left untouched."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    B, T, H = 1, 64 * 1171, 1   # 1,171 chunk-head blocks of 114,688 B > 128 MiB
+    q = torch.zeros((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    beta = torch.zeros((B, T, H), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((B, T, H, 128), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.KDAError) as e:
+        binding.chunk_fwd_noalloc(q, q, q, q, beta, o=o)
+    assert e.value.status == 6 and "scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all())
+    assert np.isfinite(host(o)).all()
