@@ -33,6 +33,11 @@ kda_status ok() {
   return KDA_OK;
 }
 
+// A launch's grid holds at most 2^32 - 1 work-items. The decode kernels run one
+// 256-work-item workgroup per (sequence, head).
+constexpr int64_t kMaxGridItems = 0xffffffffLL;
+constexpr int64_t kMaxDecodePairs = kMaxGridItems / 256;
+
 bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
 size_t dsize(kda_dtype t) { return t == KDA_F32 ? 4 : 2; }
@@ -118,6 +123,15 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
     return fail(KDA_ERR_BAD_SHAPE, "problem too large");
   if ((int64_t)n_seq * a->H * (a->dv / 16) > 0x7fffffffLL)
     return fail(KDA_ERR_BAD_SHAPE, "too many (sequence, head) pairs");
+  // the largest grid either prefill path launches (work-items): the per-(chunk, head)
+  // kernel, and the walk's (sequence, head, column strip) workgroups of up to 512 work-items,
+  // two per strip, for each of up to 15 segment walks
+  const int64_t chunks = (a->cu_seqlens ? ((int64_t)a->T + 63) / 64 + n_seq
+                                        : (int64_t)a->B * (((int64_t)a->T + 63) / 64));
+  const int64_t walk_items = ((int64_t)n_seq * a->H + 7) / 8 * 8 * (a->dv / 16) * 2 * 512 *
+                             (a->segments >= 3 ? 2 * a->segments - 3 : 1);
+  if (chunks * a->H * 256 > kMaxGridItems || walk_items > kMaxGridItems)
+    return fail(KDA_ERR_BAD_SHAPE, "the problem needs more work-items than one launch holds");
   if (a->ckpt_every < 0 || (a->ckpt_every > 0 && a->ckpt_every % a->chunk != 0))
     return fail(KDA_ERR_BAD_SHAPE, "ckpt_every must be 0 or a positive multiple of chunk (got %d)",
                 a->ckpt_every);
@@ -236,7 +250,9 @@ kda_status kda_decode_step(const kda_decode_args* a, void* hip_stream) {
     return fail(KDA_ERR_BAD_SHAPE, "need N >= 1 and H >= 1 (got N=%d H=%d)", a->N, a->H);
   if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv))
     return fail(KDA_ERR_BAD_SHAPE, "dk and dv must be 32, 64 or 128 (got %d, %d)", a->dk, a->dv);
-  if ((int64_t)a->N * a->H > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "N * H too large");
+  if ((int64_t)a->N * a->H > kMaxDecodePairs)
+    return fail(KDA_ERR_BAD_SHAPE, "N * H = %lld exceeds one launch (%lld)",
+                (long long)a->N * a->H, (long long)kMaxDecodePairs);
   if (!dtype_ok(a->act_dtype) || !dtype_ok(a->gate_dtype) || !dtype_ok(a->out_dtype))
     return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
   if (a->act_dtype != a->gate_dtype)
@@ -274,8 +290,8 @@ kda_status kda_decode_multi(const kda_decode_multi_args* a, void* hip_stream) {
     return fail(KDA_ERR_BAD_SHAPE, "need N, H, m >= 1 (got N=%d H=%d m=%d)", a->N, a->H, a->m);
   if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv))
     return fail(KDA_ERR_BAD_SHAPE, "dk and dv must be 32, 64 or 128 (got %d, %d)", a->dk, a->dv);
-  if ((int64_t)a->N * a->H > 0x7fffffffLL || (int64_t)a->N * a->m * a->H > (int64_t(1) << 40))
-    return fail(KDA_ERR_BAD_SHAPE, "N * m * H too large");
+  if ((int64_t)a->N * a->H > kMaxDecodePairs || (int64_t)a->N * a->m * a->H > (int64_t(1) << 40))
+    return fail(KDA_ERR_BAD_SHAPE, "N * H or N * m * H too large for one launch");
   if (!dtype_ok(a->act_dtype) || !dtype_ok(a->gate_dtype) || !dtype_ok(a->out_dtype))
     return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
   if (a->act_dtype != a->gate_dtype)

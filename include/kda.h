@@ -26,8 +26,13 @@
  * Conventions shared by every call
  *   - Pointers named q, k, v, g, beta, o, S0, S_T, S, workspace, cu_seqlens are DEVICE
  *     pointers (hipMalloc'ed or torch tensors); argument structs live in host memory.
- *   - The caller allocates and owns every buffer. The library keeps no device memory and
- *     no global mutable state other than a per-thread error string; it is thread safe.
+ *   - The caller allocates and owns every buffer it passes. The library allocates no device
+ *     memory; its only device memory is the fixed scratch array of kda_chunk_fwd_noalloc
+ *     (below). Its only other global state is a per-thread error string and, per device, the
+ *     looked-up address of that array; every call is thread safe except that concurrent
+ *     kda_chunk_fwd_noalloc calls on one GPU share the array.
+ *   - Sizes whose kernels would need more than 2^32 - 1 work-items in one launch are refused
+ *     with KDA_ERR_BAD_SHAPE.
  *   - Every call validates its arguments on the host, before any launch, and returns a
  *     kda_status. On failure nothing has been enqueued and kda_last_error() describes why.
  *   - Work is enqueued on the caller's HIP stream (NULL = the default stream) and the call

@@ -157,6 +157,23 @@ def test_decode_rejects_bad_args(b):
     assert b.lib().kda_decode_step(None, None) == 1
 
 
+def test_sizes_beyond_one_launch_are_refused(b):
+    """A launch grid holds at most 2^32 - 1 work-items: larger problems are refused on the host
+    with KDA_ERR_BAD_SHAPE instead of reaching the runtime with a truncated grid."""
+    a = b.DecodeArgs()
+    a.N, a.H, a.dk, a.dv = 1 << 20, 32, 128, 128   # 2^25 pairs of 256 work-items
+    a.act_dtype = a.gate_dtype = b.KDA_BF16
+    a.out_dtype = b.KDA_F32
+    a.q, a.k, a.v, a.g, a.beta = (FAKE + i * (1 << 36) for i in range(5))
+    a.S, a.o = FAKE + (6 << 36), FAKE + (7 << 36)
+    assert b.lib().kda_decode_step(ctypes.byref(a), None) == 2
+    assert "launch" in b.lib().kda_last_error().decode()
+    # prefill: 2^24 chunks of one head need 2^32 work-items in the per-chunk kernel
+    c = base_args(b, B=1 << 12, T=1 << 18, H=1, flags=b.KDA_FLAG_GENERIC)
+    assert b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(c)) == b.SIZE_MAX
+    assert "launch" in b.lib().kda_last_error().decode()
+
+
 def test_decode_multi_rejects_bad_args(b):
     a = b.DecodeMultiArgs()
     a.N, a.H, a.dk, a.dv, a.m = 4, 2, 128, 128, 3
