@@ -22,8 +22,8 @@
 //    matrix cores. Channel-major (transposed) operands come from products with an identity
 //    fragment, so no LDS staging array is needed.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
-//    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
-//    and result tiles (1 KiB = 64 lanes x 4 fp32).
+//    one coalesced load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16) and result
+//    tiles (512 B = 64 lanes x 4 fp16).
 //    A and Aqk are built from 16-token tiles whose exponent is measured from the state before
 //    the row tile: the row factor e^{G_r - ref} lies in [e^-80, 1] and the column factor
 //    e^{ref - G_j} is <= 1 off the diagonal and in [1, e^80] on it, because each step's
@@ -60,8 +60,9 @@ constexpr int OFF_PHI = 0;       // Psi as A operand: [key row tile (8)][k-step 
 constexpr int OFF_QH = 32768;    // Qhat as A operand: [k-step over dk (4)][row tile (4)]
 constexpr int OFF_Z = 49152;     // Z = Ktil^T Utilde, fp16 tiles in accumulator layout:
                                  //   [value tile (8)][key row pair (4)][lane][tile of the pair][4]
-constexpr int OFF_OH = 81920;    // Ohat result tiles, fp32: [value tile (8)][row tile (4)]
-constexpr size_t kBlockBytes = 114688;
+constexpr int OFF_OH = 81920;    // Ohat result tiles, fp16 (512 B each: 64 lanes x 4 halves):
+                                 //   [value tile (8)][row tile (4)]
+constexpr size_t kBlockBytes = 98304;
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       ao = mfma_f16(pfh[kk], vb, ao);
       ao = mfma_f16(pfl[kk], vb, ao);
     }
-    *reinterpret_cast<floatx4*>(blk + OFF_OH + (ct * 4 + w) * 1024 + l * 16) = ao;
+    *reinterpret_cast<half4*>(blk + OFF_OH + (ct * 4 + w) * 512 + l * 8) = to_half4(ao);
     if (ct & 1) {  // tiles 2kk and 2kk + 1 form the fragments of k-step kk over dk
       const int kk = ct >> 1;
       half8 qh;
@@ -799,8 +800,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
 __device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
-__device__ __forceinline__ floatx4 ld_tile(rsrc_t r, int lane_off, int off) {
-  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
+// a result tile stored in fp16 (four halves per lane), widened to the accumulator type
+__device__ __forceinline__ floatx4 ld_tile_f16(rsrc_t r, int lane_off, int off) {
+  const half4 hv = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, off, 0));
+  return floatx4{static_cast<float>(hv[0]), static_cast<float>(hv[1]), static_cast<float>(hv[2]),
+                 static_cast<float>(hv[3])};
 }
 
 // One walk of the recurrence over chunks c_lo .. c_hi - 1 of every sequence (those that exist;
@@ -1046,7 +1050,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
       for (int j = 0; j < 4; ++j) X.qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        X.oh[nt] = ld_tile(r, frag_off, OFF_OH + ((NT * sg + nt) * 4 + w) * 1024);
+        X.oh[nt] = ld_tile_f16(r, l * 8, OFF_OH + ((NT * sg + nt) * 4 + w) * 512);
     };
     auto step = [&](Ops& X, int64_t c) {
       const int bf = (int)(c & 1);

@@ -195,7 +195,7 @@ typedef struct {
 /* Bytes of device workspace kda_chunk_fwd needs for these arguments (pointers are not
  * inspected); 0 when the chosen path needs none. Validates shapes and dtypes like
  * kda_chunk_fwd and returns SIZE_MAX (with kda_last_error() set) when they are invalid.
- * The matrix-core path needs one 114,688-byte block per (chunk, head) plus small tables. */
+ * The matrix-core path needs one 98,304-byte block per (chunk, head) plus small tables. */
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* args);
 
 /* Prefill: o and S_T from q, k, v, g, beta and S0, enqueued on hip_stream (hipStream_t). */
@@ -208,7 +208,7 @@ kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
  * That scratch is a static array of the library, held by every GPU the library runs on from
  * the first use there until the process ends. Calls whose kda_chunk_fwd_workspace_bytes()
  * exceeds KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything is enqueued (at
- * most 1,170 (chunk, head) pairs of 64 tokens, e.g. 4,096 tokens with 16 heads). No device
+ * most 1,365 (chunk, head) pairs of 64 tokens, e.g. 4,096 tokens with 16 heads). No device
  * or host memory is allocated. All calls on one GPU share its scratch, whatever their stream:
  * calls that overlap in time on one GPU race (serialise them, e.g. on one stream). */
 #define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)

@@ -114,8 +114,8 @@ def test_chunk_checkpoint_rules(b):
 def test_workspace_query(b):
     q = lambda a: b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a))  # noqa: E731
     fast = q(base_args(b))
-    # one 114,688-byte block per (chunk, head): 4 chunks of 64 tokens, 4 heads
-    assert fast >= 4 * 4 * 114688
+    # one 98,304-byte block per (chunk, head): 4 chunks of 64 tokens, 4 heads
+    assert fast >= 4 * 4 * 98304
     assert q(base_args(b, flags=b.KDA_FLAG_GENERIC)) == 0
     assert q(base_args(b, act_dtype=b.KDA_F32, gate_dtype=b.KDA_F32)) == 0
     assert q(base_args(b, dk=96)) == b.SIZE_MAX and b.lib().kda_last_error()
@@ -126,10 +126,10 @@ def test_workspace_query(b):
 
 def test_noalloc_refuses_sizes_beyond_its_scratch(b):
     """kda_chunk_fwd_noalloc checks its sizes against the fixed scratch before touching a
-    device: 1,171 (chunk, head) blocks of 114,688 B exceed KDA_NOALLOC_SCRATCH_BYTES."""
+    device: 1,366 (chunk, head) blocks of 98,304 B exceed KDA_NOALLOC_SCRATCH_BYTES."""
     assert b.NOALLOC_SCRATCH_BYTES == 128 << 20
-    a = base_args(b, T=64 * 1171, H=1)
-    tok = 64 * 1171
+    a = base_args(b, T=64 * 1366, H=1)
+    tok = 64 * 1366
     a.k, a.v, a.g, a.beta = (FAKE + i * tok * 128 * 2 for i in range(1, 5))
     a.o = FAKE + (1 << 34)
     rc = b.lib().kda_chunk_fwd_noalloc(ctypes.byref(a), None)

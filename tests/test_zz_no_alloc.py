@@ -59,7 +59,7 @@ def test_noalloc_rejects_more_than_its_scratch():
     output left untouched."""
     import torch
     from gated_delta_rule_59_amd import binding
-    B, T, H = 1, 64 * 1171, 1   # 1,171 chunk-head blocks of 114,688 B > 128 MiB
+    B, T, H = 1, 64 * 1366, 1   # 1,366 chunk-head blocks of 98,304 B > 128 MiB
     q = torch.zeros((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
     beta = torch.zeros((B, T, H), dtype=torch.bfloat16, device="cuda")
     o = torch.full((B, T, H, 128), 7.0, dtype=torch.float32, device="cuda")
