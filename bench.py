@@ -333,15 +333,19 @@ def bench_segments(stream):
     S0 = torch.from_numpy(x.S0).cuda()
     o = torch.empty(q.shape[:3] + (128,), dtype=torch.float32, device="cuda")
     S_T = torch.empty_like(S0)
-    out = {"workload": "B=1 H=2 T=65536 dk=dv=128, decay floor on half the channels"}
-    for P in (0, 4, 8):
+    out = {"workload": "B=1 H=2 T=65536 dk=dv=128, decay floor on half the channels; the walk "
+                       "takes 128-token composed steps (the default for so few pairs) unless "
+                       "marked walk64"}
+    for label, P, kw in (("sequential", 0, {}), ("sequential_walk64", 0, {"walk64": True}),
+                         ("segments_4", 4, {}), ("segments_8", 8, {})):
         ws = binding.alloc_workspace(binding.chunk_fwd_workspace_bytes(q, k, v, g, beta, S0,
-                                                                       segments=P), q.device)
+                                                                       segments=P, **kw),
+                                     q.device)
         ms, n = time_window(lambda: binding.chunk_fwd(q, k, v, g, beta, S0, o=o, S_T=S_T,
-                                                      workspace=ws, stream=stream, segments=P),
-                            stream)
-        out[f"segments_{P}_event_ms" if P else "sequential_event_ms"] = ms
-        out[f"segments_{P}_launches" if P else "sequential_launches"] = n
+                                                      workspace=ws, stream=stream, segments=P,
+                                                      **kw), stream)
+        out[f"{label}_event_ms"] = ms
+        out[f"{label}_launches"] = n
     out["tokens_per_s_best"] = 65536 / (min(v for kk, v in out.items() if kk.endswith("_ms")) * 1e-3)
     return out
 

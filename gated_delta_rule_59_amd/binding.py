@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_GENERIC = 1
 KDA_FLAG_PAIRWISE_DIAG = 2
+KDA_FLAG_WALK64 = 4
+KDA_FLAG_WALK128 = 8
 ABI_VERSION = 4  # KDA_ABI_VERSION of include/kda.h this binding marshals for
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_PTR", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_DECAY_RANGE", 6: "KDA_ERR_WORKSPACE",
@@ -136,7 +138,7 @@ def _stream(stream) -> _P:
 
 def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, S_T=None,
                workspace=None, generic=False, ckpt=None, ckpt_every=0,
-               pairwise_diag=False, segments=0) -> ChunkArgs:
+               pairwise_diag=False, segments=0, walk64=False, walk128=False) -> ChunkArgs:
     B, T, H, dk = q.shape
     a = ChunkArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, v.shape[-1], chunk
@@ -149,7 +151,8 @@ def chunk_args(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64, o=None, 
     a.S0, a.o, a.S_T = _ptr(S0), _ptr(o), _ptr(S_T)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a.flags = (KDA_FLAG_GENERIC if generic else 0) | (KDA_FLAG_PAIRWISE_DIAG if pairwise_diag else 0)
+    a.flags = ((KDA_FLAG_GENERIC if generic else 0) | (KDA_FLAG_PAIRWISE_DIAG if pairwise_diag else 0)
+               | (KDA_FLAG_WALK64 if walk64 else 0) | (KDA_FLAG_WALK128 if walk128 else 0))
     a.ckpt = _ptr(ckpt)
     a.ckpt_every = ckpt_every
     a.ckpt_slots = 0 if ckpt is None else ckpt.shape[0]
@@ -164,9 +167,10 @@ def checkpoint_slots(lengths, every: int) -> int:
 
 
 def chunk_fwd_workspace_bytes(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
-                              generic=False, segments=0) -> int:
+                              generic=False, segments=0, walk64=False, walk128=False,
+                              ckpt_every=0) -> int:
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, generic=generic,
-                   segments=segments)
+                   segments=segments, walk64=walk64, walk128=walk128, ckpt_every=ckpt_every)
     n = lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a))
     if n == SIZE_MAX:
         raise KDAError(2, lib().kda_last_error().decode())
@@ -183,7 +187,7 @@ def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
               out_dtype=torch.float32, o=None, S_T=None, want_state=True, workspace=None,
               generic=False, stream=None, ckpt=None, ckpt_every=0, pairwise_diag=False,
-              segments=0):
+              segments=0, walk64=False, walk128=False):
     """Prefill. q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H] (bf16 or fp32, on the
     GPU, contiguous); S0 [n_seq, H, dk, dv] fp32 or None; cu_seqlens int32 [N + 1] or None.
     Returns (o [B, T, H, dv] out_dtype, S_T [n_seq, H, dk, dv] fp32 or None).
@@ -191,7 +195,9 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
     ckpt_every > 0 (a multiple of chunk) also stores the state after every ckpt_every tokens
     of each sequence into ckpt [slots, H, dk, dv] fp32 (see checkpoint_slots).
     pairwise_diag evaluates the diagonal tiles pairwise (no lower bound on g needed; slower).
-    segments (3 .. 8) walks each sequence in that many segments in parallel (see kda.h)."""
+    segments (3 .. 8) walks each sequence in that many segments in parallel (see kda.h).
+    walk64 / walk128 make the matrix-core walk take one 64-token chunk per step, or two
+    chunks composed into one 128-token step (see kda.h; by default the library chooses)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     if S0 is not None:
@@ -211,7 +217,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
         S_T = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         nbytes = chunk_fwd_workspace_bytes(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk,
-                                           generic=generic, segments=segments)
+                                           generic=generic, segments=segments, walk64=walk64,
+                                           walk128=walk128, ckpt_every=ckpt_every)
         workspace = alloc_workspace(nbytes, q.device)
     if ckpt_every:
         if ckpt is None:
@@ -221,13 +228,15 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, chunk=64,
             raise ValueError("ckpt must be fp32 [slots, H, dk, dv]")
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
                    workspace=workspace, generic=generic, ckpt=ckpt if ckpt_every else None,
-                   ckpt_every=ckpt_every, pairwise_diag=pairwise_diag, segments=segments)
+                   ckpt_every=ckpt_every, pairwise_diag=pairwise_diag, segments=segments,
+                   walk64=walk64, walk128=walk128)
     _check(lib().kda_chunk_fwd(ctypes.byref(a), _stream(stream)))
     return o, S_T
 
 
 def chunk_fwd_noalloc(q, k, v, g, beta, S0=None, cu_seqlens=None, *, o, S_T=None, chunk=64,
-                      generic=False, stream=None, ckpt=None, ckpt_every=0, segments=0):
+                      generic=False, stream=None, ckpt=None, ckpt_every=0, segments=0,
+                      walk64=False, walk128=False):
     """kda_chunk_fwd_noalloc: the prefill with the library's fixed device scratch in place of
     a workspace; o (and S_T, ckpt when wanted) are the caller's, nothing is allocated here.
     Raises KDAError (KDA_ERR_WORKSPACE) when the sizes need more than NOALLOC_SCRATCH_BYTES."""
@@ -238,7 +247,7 @@ def chunk_fwd_noalloc(q, k, v, g, beta, S0=None, cu_seqlens=None, *, o, S_T=None
             _dev(t, name)
     a = chunk_args(q, k, v, g, beta, S0, cu_seqlens, chunk=chunk, o=o, S_T=S_T,
                    generic=generic, ckpt=ckpt if ckpt_every else None, ckpt_every=ckpt_every,
-                   segments=segments)
+                   segments=segments, walk64=walk64, walk128=walk128)
     _check(lib().kda_chunk_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return o, S_T
 

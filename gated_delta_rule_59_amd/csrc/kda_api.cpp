@@ -97,7 +97,21 @@ kda_status env_gate_check(const void* g, int64_t n_g, const void* beta, int64_t 
   return KDA_OK;
 }
 
-// Shape/dtype validation shared by kda_chunk_fwd and kda_chunk_fwd_workspace.
+// Tokens per step of the matrix-core walk. Two chunks composed into one 128-token step halve
+// the serial steps and the workspace bytes, but the composition costs the parallel part about
+// 30 % more; measured on MI355X it pays where the walk dominates, i.e. few (sequence, head)
+// pairs (one 65,536-token sequence: 0.708 -> 0.446 ms with 2 heads, 1.12 -> 1.00 ms with 8),
+// and is even with 16 or 32 heads. One chunk per step when asked, and whenever checkpoints fall
+// between 128-token steps (decided from ckpt_every alone, so that the workspace size does not
+// depend on ckpt_slots).
+constexpr int kComposeMaxPairs = 8;
+int walk_block(const kda_chunk_args* a, int n_seq) {
+  if ((a->flags & KDA_FLAG_WALK64) || (a->ckpt_every > 0 && a->ckpt_every % 128 != 0)) return 64;
+  if (a->flags & KDA_FLAG_WALK128) return 128;
+  return (int64_t)n_seq * a->H <= kComposeMaxPairs ? 128 : 64;
+}
+
+// Shape/dtype validation shared by kda_chunk_fwd and kda_chunk_fwd_workspace_bytes.
 kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
   if (!a) return fail(KDA_ERR_NULL_PTR, "args is NULL");
   if (a->B < 1 || a->T < 0 || a->H < 1)
@@ -115,8 +129,14 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
     return fail(KDA_ERR_BAD_DTYPE, "unknown dtype");
   if (a->act_dtype != a->gate_dtype)
     return fail(KDA_ERR_BAD_DTYPE, "act_dtype and gate_dtype must match (both F32 or both BF16)");
-  if (a->flags & ~(KDA_FLAG_GENERIC | KDA_FLAG_PAIRWISE_DIAG))
+  if (a->flags & ~(KDA_FLAG_GENERIC | KDA_FLAG_PAIRWISE_DIAG | KDA_FLAG_WALK64 | KDA_FLAG_WALK128))
     return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags);
+  if ((a->flags & KDA_FLAG_WALK64) && (a->flags & KDA_FLAG_WALK128))
+    return fail(KDA_ERR_UNSUPPORTED, "KDA_FLAG_WALK64 and KDA_FLAG_WALK128 exclude each other");
+  if ((a->flags & KDA_FLAG_WALK128) && a->ckpt_every > 0 && a->ckpt_every % 128 != 0)
+    return fail(KDA_ERR_UNSUPPORTED,
+                "KDA_FLAG_WALK128: checkpoints every %d tokens fall between 128-token steps",
+                a->ckpt_every);
   const int64_t tokens = (int64_t)a->B * a->T;
   const int n_seq = a->cu_seqlens ? a->N : a->B;
   if (tokens * a->H * (int64_t)(a->dk > a->dv ? a->dk : a->dv) > (int64_t(1) << 40))
@@ -145,7 +165,8 @@ kda_status validate_chunk_shapes(const kda_chunk_args* a, kda::ChunkPlan* p) {
                       a->q, a->k, a->v, a->g, a->beta, a->S0, a->o, a->S_T,
                       a->workspace, a->workspace_bytes,
                       ck ? a->ckpt : nullptr, ck ? a->ckpt_every : 0, ck ? a->ckpt_slots : 0,
-                      (a->flags & KDA_FLAG_PAIRWISE_DIAG) != 0, a->segments};
+                      (a->flags & KDA_FLAG_PAIRWISE_DIAG) != 0, a->segments,
+                      walk_block(a, n_seq)};
   return KDA_OK;
 }
 

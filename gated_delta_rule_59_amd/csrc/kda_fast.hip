@@ -22,8 +22,8 @@
 //    matrix cores. Channel-major (transposed) operands come from products with an identity
 //    fragment, so no LDS staging array is needed.
 //    Results are stored in the workspace already in MFMA lane order, so each later load is
-//    one coalesced load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16) and result
-//    tiles (512 B = 64 lanes x 4 fp16).
+//    one coalesced 16-byte load per lane: operand "fragments" (1 KiB = 64 lanes x 8 fp16)
+//    and result tiles (1 KiB = 64 lanes x 4 fp32).
 //    A and Aqk are built from 16-token tiles whose exponent is measured from the state before
 //    the row tile: the row factor e^{G_r - ref} lies in [e^-80, 1] and the column factor
 //    e^{ref - G_j} is <= 1 off the diagonal and in [1, e^80] on it, because each step's
@@ -54,23 +54,34 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int NSTRIP = DV / 16;  // 16-column strips per (sequence, head)
 
-// Workspace block of one (chunk, head), byte offsets. Fragment f of a group starts at
-// group + f * 1024 (lane l's eight fp16 at + l * 16); result tile f likewise (four fp32).
-constexpr int OFF_PHI = 0;       // Psi as A operand: [key row tile (8)][k-step over keys (4)]
-constexpr int OFF_QH = 32768;    // Qhat as A operand: [k-step over dk (4)][row tile (4)]
-constexpr int OFF_Z = 49152;     // Z = Ktil^T Utilde, fp16 tiles in accumulator layout:
-                                 //   [value tile (8)][key row pair (4)][lane][tile of the pair][4]
-constexpr int OFF_OH = 81920;    // Ohat result tiles, fp16 (512 B each: 64 lanes x 4 halves):
-                                 //   [value tile (8)][row tile (4)]
-constexpr size_t kBlockBytes = 98304;
+// Workspace block of BL tokens of one head, byte offsets: BL = 64 holds one chunk, BL = 128
+// two consecutive chunks composed into one step of the walk. Fragment f of a group starts at
+// group + f * 1024 (lane l's eight fp16 at + l * 16); a result tile f likewise (four fp32).
+//   phi  Psi as A operand: [key row tile (8)][k-step over keys (4)]                 32 KiB
+//   qh   Qhat as A operand: [k-step over dk (4)][row tile (BL / 16)]      4 KiB per row tile
+//   z    Z, fp16 tiles in accumulator layout:
+//        [value tile (8)][key row pair (4)][lane][tile of the pair][4]              32 KiB
+//   oh   Ohat result tiles, fp32: [value tile (8)][row tile (BL / 16)]    8 KiB per row tile
+// Ohat stays fp32: the largest outputs reach tens of times their RMS, and fp16 rounding of
+// Ohat alone put half of the 2e-2 max-abs budget on the long workloads.
+struct Layout {
+  int phi, qh, z, oh, block;
+};
+constexpr Layout layout(int BL) {
+  return Layout{0, 32768, 32768 + (BL / 16) * 4096, 65536 + (BL / 16) * 4096,
+                65536 + (BL / 16) * 12288};
+}
+static_assert(layout(64).block == 114688 && layout(128).block == 163840, "block sizes");
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
   int64_t len;
-  int64_t cid0;  // first chunk of the sequence in the workspace
+  int64_t cid0;  // first block of the sequence in the workspace
 };
 
-__device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int32_t* chunk_off,
+// sequence n's tokens, and its first workspace block of BL tokens
+template <int BL>
+__device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int32_t* blk_off,
                                             int T) {
   SeqInfo s;
   if (cu) {
@@ -78,23 +89,25 @@ __device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int3
     const int64_t e = min(max((int64_t)cu[n + 1], a), (int64_t)T);
     s.tok0 = a;
     s.len = e - a;
-    s.cid0 = chunk_off[n];
+    s.cid0 = blk_off[n];
   } else {
     s.tok0 = (int64_t)n * T;
     s.len = T;
-    s.cid0 = (int64_t)n * ((T + C - 1) / C);
+    s.cid0 = (int64_t)n * ((T + BL - 1) / BL);
   }
   return s;
 }
 
-// chunk_off[n] = number of chunks of sequences 0..n-1 (lengths clamped as in seq_info), and,
+// blk_off[n] = number of blocks of blk_len tokens of sequences 0..n-1 (lengths clamped as in
+// seq_info), and,
 // when every > 0, ckpt_off[n] = number of state checkpoints of sequences 0..n-1 (one per full
 // `every` tokens of each). order[] lists the sequences longest first (ties by index) when
-// there are at most kMaxOrdered of them, else in their own order: the chunk walks are then
+// there are at most kMaxOrdered of them, else in their own order: the walks are then
 // dispatched longest first, so the longest ones do not start last and set the tail.
 constexpr int kMaxOrdered = 512;
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int n_seq,
-                                                   int T, int every, int32_t* __restrict__ chunk_off,
+                                                   int T, int blk_len, int every,
+                                                   int32_t* __restrict__ blk_off,
                                                    int32_t* __restrict__ ckpt_off,
                                                    int32_t* __restrict__ order) {
   __shared__ int64_t part[2][256];
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
   int64_t sum = 0, sck = 0;
   for (int n = lo; n < hi; ++n) {
     const int64_t len = seq_len(n);
-    sum += (len + C - 1) / C;
+    sum += (len + blk_len - 1) / blk_len;
     if (every > 0) sck += len / every;
   }
   part[0][t] = sum;
@@ -127,14 +140,14 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
   int64_t acc = part[0][t], ack = part[1][t];
   for (int n = lo; n < hi; ++n) {
     const int64_t len = seq_len(n);
-    chunk_off[n] = (int32_t)acc;
-    acc += (len + C - 1) / C;
+    blk_off[n] = (int32_t)acc;
+    acc += (len + blk_len - 1) / blk_len;
     if (every > 0) {
       ckpt_off[n] = (int32_t)ack;
       ack += len / every;
     }
   }
-  if (t == 255) chunk_off[n_seq] = (int32_t)acc;
+  if (t == 255) blk_off[n_seq] = (int32_t)acc;
   for (int n = lo; n < hi; ++n) {  // the rank of n is its slot: a permutation of 0..n_seq-1
     int rank = n;
     if (n_seq <= kMaxOrdered) {
@@ -234,12 +247,15 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 // PAIRWISE replaces the dense diagonal tiles by the pairwise evaluation of the earlier
 // generation (each e^{G_r - G_j} formed per pair and channel, in fp32 on the vector ALUs),
 // which needs no bound on the decay: the ablation that measures what the bound buys.
-template <bool PAIRWISE>
-__global__ __launch_bounds__(256, 2) void prep_kernel(
+template <bool PAIRWISE, bool COMPOSE>
+__global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, int T, int H,
-    int n_seq, uint8_t* __restrict__ ws, int c_lo, int c_span) {
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ blk_off, int T, int H,
+    int n_seq, uint8_t* __restrict__ ws) {
+  constexpr int BL = COMPOSE ? 2 * C : C;  // tokens per workspace block
+  constexpr int NGRP = COMPOSE ? 2 : 1;    // groups of four waves, one chunk each
+  constexpr Layout LY = layout(BL);
   constexpr int AS = C + 4;  // row stride (fp32) of A and T
   // One LDS arena reused phase by phase (byte ranges), 66 KB, two workgroups per CU (the
   // kernel needs about 190 registers; at three workgroups it spilled, and every spill reload
@@ -257,9 +273,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   constexpr int OFF_TAB = PAIRWISE ? 4 * PW_WAVE : 24576;
   constexpr int OFF_KBF = 34816, OFF_KTL = 51200;
   constexpr int ARENA = PAIRWISE ? OFF_TAB + 7680 : 67584;
-  __shared__ __align__(16) unsigned char arena[ARENA];
-  __shared__ __align__(16) float Bs[C];
-  __shared__ float GAMS[DK];  // e^{G_C} per key channel, for the diagonal of Psi
+  __shared__ __align__(16) unsigned char arenas[NGRP][ARENA];
+  __shared__ __align__(16) float Bss[NGRP][C];
+  __shared__ float GAMSS[NGRP][DK];  // e^{G_C} per key channel, for the diagonal of Psi
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = wave >> 2;  // which chunk of the block this wave works on
+  const int w = wave & 3;
+  unsigned char* arena = arenas[grp];
+  float* Bs = Bss[grp];
+  float* GAMS = GAMSS[grp];
   float* KC = reinterpret_cast<float*>(arena);
   float(*TOT)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB);
   float(*PCH)[DK] = reinterpret_cast<float(*)[DK]>(arena + OFF_TAB + 2048);
@@ -274,32 +298,35 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   static_assert(OFF_KTL + 16384 <= ARENA && (PAIRWISE || OFF_TAB + 7680 <= OFF_KBF), "layout");
   static_assert(4 * PW_WAVE <= (PAIRWISE ? ARENA : 1 << 30), "layout");
 
+  // one workgroup per (block, head); the whole workgroup leaves together, so that the
+  // barriers below always see every wave
   const int h = blockIdx.x % H;
-  const int64_t cid = blockIdx.x / H;
+  const int64_t bid = blockIdx.x / H;
   int n;
-  int64_t c_in;
+  int64_t b_in;
   if (cu) {
-    if (cid >= chunk_off[n_seq]) return;
-    int lo = 0, hi = n_seq - 1;  // last n with chunk_off[n] <= cid
+    if (bid >= blk_off[n_seq]) return;
+    int lo = 0, hi = n_seq - 1;  // last n with blk_off[n] <= bid
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (chunk_off[mid] <= cid) lo = mid; else hi = mid - 1;
+      if (blk_off[mid] <= bid) lo = mid; else hi = mid - 1;
     }
     n = lo;
-    c_in = cid - chunk_off[n];
-  } else {  // dense batch: chunks c_lo .. c_lo + c_span - 1 of every sequence
-    const int64_t ncs = (T + C - 1) / C;
-    n = (int)(cid / c_span);
-    c_in = c_lo + cid % c_span;
-    if (n >= n_seq || c_in >= ncs) return;
+    b_in = bid - blk_off[n];
+  } else {  // dense batch
+    const int64_t nbs = (T + BL - 1) / BL;
+    n = (int)(bid / nbs);
+    b_in = bid % nbs;
+    if (n >= n_seq) return;
   }
-  const SeqInfo si = seq_info(n, cu, chunk_off, T);
+  const SeqInfo si = seq_info<BL>(n, cu, blk_off, T);
+  // this group's chunk; the second chunk of a sequence's last block may hold no token (then
+  // every load below reads zero and the chunk is the identity transition)
+  const int64_t c_in = b_in * NGRP + grp;
   const int64_t tok0 = si.tok0 + c_in * C;
-  const int Cn = (int)min((int64_t)C, si.len - c_in * C);
-  uint8_t* blk = ws + ((size_t)(si.cid0 + c_in) * H + h) * kBlockBytes;
+  const int Cn = (int)max((int64_t)0, min((int64_t)C, si.len - c_in * C));
+  uint8_t* blk = ws + ((size_t)(si.cid0 + b_in) * H + h) * LY.block;
 
-  const int t = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l = t & 63, gq = l >> 4, m = l & 15;
   const int row = 16 * w + m;
 
@@ -366,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   __syncthreads();
   // ---- per-channel constants from the tile totals (half the threads per pair of tiles)
   {
-    const int c = t & (DK - 1), hf = t >> 7;
+    const int c = t & (DK - 1), hf = (t >> 7) & 1;  // this group's 256 threads
     const float t0 = TOT[0][c], t1 = TOT[1][c], t2 = TOT[2][c], t3 = TOT[3][c];
     const float ref[4] = {0.f, t0, t0 + t1, t0 + t1 + t2};
     const float tt[4] = {t0, t1, t2, t3};
@@ -685,7 +712,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
   }
   __syncthreads();
   // ---- row tile w: (P Kbar)^T = Kbar^T P^T, so that Qhat = Qbar - P Kbar comes out as
-  //      A-operand fragments, and Ohat = P V as result tiles in the walk's accumulator layout
+  //      A-operand fragments, and Ohat = P V as result tiles in the walk's accumulator layout.
+  //      The second chunk of a composed block keeps both in registers for the composition.
+  constexpr int RTB = BL / 16;  // row tiles of a block
+  const bool second = COMPOSE && grp == 1;
+  floatx4 ohb[8];  // second chunk: Ohat of row tile w, value tiles 0..7
+  half8 qhb[4];    // second chunk: Qhat fragments of row tile w, k-steps 0..3
   floatx4 pk_prev = zero;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
@@ -699,14 +731,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       ao = mfma_f16(pfh[kk], vb, ao);
       ao = mfma_f16(pfl[kk], vb, ao);
     }
-    *reinterpret_cast<half4*>(blk + OFF_OH + (ct * 4 + w) * 512 + l * 8) = to_half4(ao);
+    if (second)
+      ohb[ct] = ao;
+    else
+      *reinterpret_cast<floatx4*>(blk + LY.oh + (ct * RTB + w) * 1024 + l * 16) = ao;
     if (ct & 1) {  // tiles 2kk and 2kk + 1 form the fragments of k-step kk over dk
       const int kk = ct >> 1;
       half8 qh;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qh[i] = static_cast<_Float16>(static_cast<float>(qbar[kk][i]) - (i < 4 ? pk_prev[i] : ap[i - 4]));
-      *reinterpret_cast<half8*>(blk + OFF_QH + (kk * 4 + w) * 1024 + l * 16) = qh;
+      if (second)
+        qhb[kk] = qh;
+      else
+        *reinterpret_cast<half8*>(blk + LY.qh + (kk * RTB + w) * 1024 + l * 16) = qh;
     }
     pk_prev = ap;
   }
@@ -749,8 +787,29 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       }
     }
   }
+  // ---- composing a block: the two chunks hand each other their parts through staging areas
+  //      in the parts of the arenas that only the products above read (V, M and Kbar^T;
+  //      Ktil^T, still needed for Z, lies above them):
+  //        PB  Psi of the second chunk, row fragments [key row tile][k-step]    arena 1 + 17408
+  //        QB  Qhat of the second chunk, fragments [k-step][row tile]             arena 1 + 0
+  //        ZA  Z of the first chunk, B-operand fragments [value tile][key pair]   arena 0 + 0
+  half8* const PB = reinterpret_cast<half8*>(arenas[NGRP - 1] + 17408);
+  half8* const QB = reinterpret_cast<half8*>(arenas[NGRP - 1]);
+  half8* const ZA = reinterpret_cast<half8*>(arenas[0]);
+  static_assert(17408 + 32768 <= OFF_KTL && 16384 <= 17408 && 32768 <= OFF_KTL, "staging");
+  if constexpr (COMPOSE) {
+    __syncthreads();  // every wave is past its last read of V, M and Kbar^T
+    if (second) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) QB[(kk * 4 + w) * 64 + l] = qhb[kk];
+    }
+  }
   // ---- Phi = Ktil^T W for key rows kt and key columns 32w .. 32w + 31, computed as
-  //      Phi^T = W^T Ktil so that each lane ends with its own row: A-operand fragments (kt, w)
+  //      Phi^T = W^T Ktil so that each lane ends with its own row: A-operand fragments (kt, w).
+  //      The first chunk of a composed block also forms Phi itself, whose result tiles are
+  //      column fragments (a lane holds four rows of one column): the composition's A operand.
+  half8 pra[8];     // first chunk: Psi row fragments (kt, w)
+  half8 pca[2][4];  // first chunk: Psi column fragments (column tile 2w + tc, k-step over rows)
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
     floatx4 d0 = zero, d1 = zero;
@@ -770,10 +829,33 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
       ph[i] = static_cast<_Float16>(-d0[i] - (i == dslot ? dlt : 0.f));
       ph[i + 4] = static_cast<_Float16>(-d1[i] - (i + 4 == dslot ? dlt : 0.f));
     }
-    *reinterpret_cast<half8*>(blk + OFF_PHI + (kt * 4 + w) * 1024 + l * 16) = ph;
+    if (!COMPOSE)
+      *reinterpret_cast<half8*>(blk + LY.phi + (kt * 4 + w) * 1024 + l * 16) = ph;
+    else if (second)
+      PB[(kt * 4 + w) * 64 + l] = ph;
+    else
+      pra[kt] = ph;
+    if (COMPOSE && !second) {
+      // tile (kt, 2w + tc) of Phi: the lane holds column 16 (2w + tc) + m, rows 16 kt + 4 gq + i,
+      // the diagonal where 16 kt + 4 gq + i = 16 (2w + tc) + m
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        floatx4 e = zero;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) e = mfma_f16(KTL[(kt * 2 + kk) * 64 + l], wb[tc][kk], e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool diag = kt == 2 * w + tc && 4 * gq + i == m;
+          pca[tc][kt >> 1][4 * (kt & 1) + i] =
+              static_cast<_Float16>(-e[i] - (diag ? 1.f - GAMS[16 * kt + m] : 0.f));
+        }
+      }
+    }
   }
   // ---- Z = Ktil^T Utilde for value tiles 2w and 2w + 1, every key row tile: the lane holds
-  //      key rows 16 kt + 4 gq + i of value column m, the walk's accumulator layout (fp16)
+  //      key rows 16 kt + 4 gq + i of value column m, the walk's accumulator layout (fp16).
+  //      Composing: the first chunk's Z goes to ZA, the second chunk's stays in fp32 registers.
+  floatx4 zb[2][8];  // second chunk: Z tiles (value tile 2w + tt, key row tile kt)
 #pragma unroll
   for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
@@ -788,23 +870,128 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         dz2 = mfma_f16(kf0, ul[tt][0], dz2);
         dz = mfma_f16(kf1, uh[tt][1], dz);
         dz2 = mfma_f16(kf1, ul[tt][1], dz2);
+        if (second) zb[tt][kt] = dz + dz2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) zf[4 * u + i] = static_cast<_Float16>(dz[i] + dz2[i]);
       }
       const int vt = 2 * w + tt;
-      *reinterpret_cast<half8*>(blk + OFF_Z + ((vt * 4 + kp) * 64 + l) * 16) = zf;
+      if (!COMPOSE)
+        *reinterpret_cast<half8*>(blk + LY.z + ((vt * 4 + kp) * 64 + l) * 16) = zf;
+      else if (!second)
+        ZA[(vt * 4 + kp) * 64 + l] = zf;
     }
+  if constexpr (COMPOSE) {
+    // ---- the block's step from the two chunks' steps S -> S + Z + Psi S:
+    //        Psi'    = Psi_a + Psi_b + Psi_b Psi_a
+    //        Z'      = Z_a + Z_b + Psi_b Z_a
+    //        Qhat'_b = Qhat_b + Qhat_b Psi_a,   Ohat'_b = Ohat_b + Qhat_b Z_a
+    //      (the second chunk's outputs read the state entering the block); the first chunk's
+    //      Qhat and Ohat are stored as they are.
+    __syncthreads();  // PB, QB and ZA are complete
+    if (!second) {
+      // Psi' row fragments (kt, w) as the transposed product Psi_a^T Psi_b^T: each lane ends
+      // with four entries of its own row of Psi' per 16-column tile 2w + tc
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        half8 pb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pb[ks] = PB[(kt * 4 + ks) * 64 + l];
+        const half8 pbw = w == 0 ? pb[0] : w == 1 ? pb[1] : w == 2 ? pb[2] : pb[3];  // seed (kt, w)
+        floatx4 acc[2];
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[tc][i] = static_cast<float>(pra[kt][4 * tc + i]) + static_cast<float>(pbw[4 * tc + i]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int tc = 0; tc < 2; ++tc) acc[tc] = mfma_f16(pca[tc][ks], pb[ks], acc[tc]);
+        half8 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          out[i] = static_cast<_Float16>(acc[0][i]);
+          out[i + 4] = static_cast<_Float16>(acc[1][i]);
+        }
+        *reinterpret_cast<half8*>(blk + LY.phi + (kt * 4 + w) * 1024 + l * 16) = out;
+      }
+      // Qhat'_b fragments (k-step w, row tile rt of the second chunk), transposed likewise
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        half8 qb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = QB[(ks * 4 + rt) * 64 + l];
+        const half8 qbw = w == 0 ? qb[0] : w == 1 ? qb[1] : w == 2 ? qb[2] : qb[3];  // seed (w, rt)
+        floatx4 acc[2];
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tc][i] = static_cast<float>(qbw[4 * tc + i]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int tc = 0; tc < 2; ++tc) acc[tc] = mfma_f16(pca[tc][ks], qb[ks], acc[tc]);
+        half8 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          out[i] = static_cast<_Float16>(acc[0][i]);
+          out[i + 4] = static_cast<_Float16>(acc[1][i]);
+        }
+        *reinterpret_cast<half8*>(blk + LY.qh + (w * RTB + 4 + rt) * 1024 + l * 16) = out;
+      }
+    } else {
+      // Z' tiles (key row tile r, value tile 2w + tt), in the walk's layout. Z_a's fragments
+      // of this wave's two value tiles stay in registers; each Psi_b fragment is read once.
+      half8 za[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) za[tt][ks] = ZA[((2 * w + tt) * 4 + ks) * 64 + l];
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        half8 zo[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 2 * kp + u;
+          half8 pb[4];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) pb[ks] = PB[(r * 4 + ks) * 64 + l];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            floatx4 acc = zb[tt][r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += static_cast<float>(za[tt][kp][4 * u + i]);  // Z_a
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma_f16(pb[ks], za[tt][ks], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zo[tt][4 * u + i] = static_cast<_Float16>(acc[i]);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          *reinterpret_cast<half8*>(blk + LY.z + (((2 * w + tt) * 4 + kp) * 64 + l) * 16) = zo[tt];
+      }
+      // Ohat'_b tiles (value tile vt, row tile w of the second chunk)
+#pragma unroll
+      for (int vt = 0; vt < 8; ++vt) {
+        floatx4 acc = ohb[vt];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bool mine = (vt >> 1) == w;  // already in registers
+          acc = mfma_f16(qhb[ks], mine ? za[vt & 1][ks] : ZA[(vt * 4 + ks) * 64 + l], acc);
+        }
+        *reinterpret_cast<floatx4*>(blk + LY.oh + (vt * RTB + 4 + w) * 1024 + l * 16) = acc;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- rec
 __device__ __forceinline__ half8 ld_frag(rsrc_t r, int lane_off, int off) {
   return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
-// a result tile stored in fp16 (four halves per lane), widened to the accumulator type
-__device__ __forceinline__ floatx4 ld_tile_f16(rsrc_t r, int lane_off, int off) {
-  const half4 hv = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, off, 0));
-  return floatx4{static_cast<float>(hv[0]), static_cast<float>(hv[1]), static_cast<float>(hv[2]),
-                 static_cast<float>(hv[3])};
+__device__ __forceinline__ floatx4 ld_tile(rsrc_t r, int lane_off, int off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, off, 0));
 }
 
 // One walk of the recurrence over chunks c_lo .. c_hi - 1 of every sequence (those that exist;
@@ -830,7 +1017,16 @@ struct RecJobs {
                // half of the chunk rows (fewer operand bytes per CU when CUs would be idle)
 };
 
-template <typename TOut, int NT>
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// The walk steps over workspace blocks of BL tokens (one chunk of 64, or two composed into
+// 128); below, "chunk" c is such a block. CKPT: the launch stores state checkpoints (a kernel
+// of its own, so that the plain walk's loop holds no conditional stores: the compiler would
+// otherwise drain every load in flight at their merge, once per unrolled loop trip).
+template <typename TOut, int NT, int BL, bool CKPT>
 __global__ __launch_bounds__(512) void rec_kernel(
     RecJobs jobs, TOut* __restrict__ o, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_off, int T, int H, int n_seq, int64_t max_chunks,
@@ -844,6 +1040,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // rows padded by 8 halves against bank conflicts, in two buffers used by alternate chunks:
   // the buffer of chunk c is read between barrier c and barrier c + 1, and written again only
   // for chunk c + 2, after barrier c + 1.
+  constexpr Layout LY = layout(BL);
+  constexpr int RT = BL / 16;      // row tiles of a chunk
   constexpr int NG = NSTRIP / NT;  // strip groups per (sequence, head)
   constexpr int SR = DK + 8;
   __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];
@@ -862,9 +1060,9 @@ __global__ __launch_bounds__(512) void rec_kernel(
   if (pair >= (int64_t)n_seq * H) return;
   // packed sequences are walked longest first (order from the plan kernel)
   const int n = order ? order[pair / H] : (int)(pair / H), h = (int)(pair % H);
-  const SeqInfo si = seq_info(n, cu, chunk_off, T);
+  const SeqInfo si = seq_info<BL>(n, cu, chunk_off, T);
   // a malformed cu_seqlens cannot make the chunk walk leave the workspace
-  const int64_t nc = max((int64_t)0, min((si.len + C - 1) / C, max_chunks - si.cid0));
+  const int64_t nc = max((int64_t)0, min((si.len + BL - 1) / BL, max_chunks - si.cid0));
   const int64_t c_end = min(nc, c_hi);  // this launch walks chunks c_lo .. c_end - 1
 
   const int t = threadIdx.x;
@@ -872,19 +1070,99 @@ __global__ __launch_bounds__(512) void rec_kernel(
   const int w = wave & 3;
   const int l = t & 63, gq = l >> 4, nn = l & 15;
   const int frag_off = l * 16;
-  const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * kBlockBytes;
-  const size_t blk_step = (size_t)H * kBlockBytes;
+  const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * LY.block;
+  const size_t blk_step = (size_t)H * LY.block;
 
   // B operand of state strip nt for key rows 32 j + kslot(gq, i), column nn, from buffer bf
   auto state_frag = [&](int bf, int nt, int j) { return lds_frag(&sx[bf][16 * nt + nn][32 * j], gq); };
   // first checkpoint slot of this sequence (checkpoints every ckpt_chunks full chunks)
   const int64_t ck_base =
-      ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * C))) : 0;
+      ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * BL))) : 0;
   // the second workgroup of a split pair repeats the walk: only the first writes states. Both
   // read S0 when they start, so the split assumes S0 is not written during the launch (the
   // host never splits an in-place walk, where S_T is the S0 buffer).
-  const int ck_every = job.mode == REC_OUTPUT && half == 0 ? ckpt_chunks : 0;
+  const int ck_every = CKPT && job.mode == REC_OUTPUT && half == 0 ? ckpt_chunks : 0;
   if (half != 0) S_T = nullptr;
+
+  // ------------------------------------------------ output waves: chunk rows of JN row tiles
+  // (rt0, and rt1 when JN = 2), o = Qhat S + Ohat from the state entering the chunk. The tile
+  // count is a compile-time constant, so that the loop holds no branch around its loads and
+  // the compiler keeps its waits partial (two chunks of operands in flight).
+  auto out_waves = [&](auto jn, int rt0, int rt1) {
+    constexpr int JN = decltype(jn)::value;
+    const int rts[2] = {rt0, rt1};
+    const int row_stride = H * DV;  // elements between consecutive tokens
+    int o_off[JN][NT][4];
+#pragma unroll
+    for (int j = 0; j < JN; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o_off[j][nt][i] = ((16 * rts[j] + 4 * gq + i) * row_stride + 16 * (NT * sg + nt) + nn) *
+                            (int)sizeof(TOut);
+    TOut* o_base = o + (si.tok0 * H + h) * DV;
+    const size_t tok_step = (size_t)BL * row_stride;
+    struct Ops {
+      half8 qh[JN][4];
+      floatx4 oh[JN][NT];
+    };
+    Ops A, B;
+    auto load_q = [&](Ops& X, int64_t c) {
+      const rsrc_t r = make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)LY.block);
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) X.qh[j][ks] = ld_frag(r, frag_off, LY.qh + (ks * RT + rts[j]) * 1024);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          X.oh[j][nt] = ld_tile(r, frag_off, LY.oh + ((NT * sg + nt) * RT + rts[j]) * 1024);
+      }
+    };
+    auto step = [&](Ops& X, int64_t c) {
+      const int bf = (int)(c & 1);
+      __syncthreads();
+      // the products read the state entering the chunk, from the buffer the state waves
+      // filled before this barrier
+      floatx4 acc[JN][NT];
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          floatx4 a0 = mfma_f16(X.qh[j][0], state_frag(bf, nt, 0), X.oh[j][nt]);
+          floatx4 a1 = mfma_f16(X.qh[j][2], state_frag(bf, nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
+          a0 = mfma_f16(X.qh[j][1], state_frag(bf, nt, 1), a0);
+          a1 = mfma_f16(X.qh[j][3], state_frag(bf, nt, 3), a1);
+          acc[j][nt] = a0 + a1;
+        }
+      load_q(X, c + 2);
+      // bytes of the chunk's rows of this head, up to the end of its last valid row
+      const int64_t rows = min((int64_t)BL, si.len - c * BL);
+      const rsrc_t ro = make_rsrc(o_base + c * tok_step, ((rows - 1) * row_stride + DV) * (int64_t)sizeof(TOut));
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (sizeof(TOut) == 4)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][nt][i]), ro, o_off[j][nt][i], 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[j][nt][i]), ro, o_off[j][nt][i], 0, 0);
+          }
+    };
+    if (c_end > c_lo) {
+      load_q(A, c_lo);
+      load_q(B, c_lo + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
+    int64_t c = c_lo;
+    for (; c + 1 < c_end; c += 2) {
+      step(A, c);
+      step(B, c + 1);
+    }
+    if (c < c_end) step(A, c);
+  };
 
   if (wave < 4) {
     // ------------------------------------------------ state waves: key rows 32w .. 32w+31
@@ -921,19 +1199,19 @@ __global__ __launch_bounds__(512) void rec_kernel(
     auto load_part = [&](Ops& X, rsrc_t r, int part) {
       if (part < 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) X.phi[part][j] = ld_frag(r, frag_off, OFF_PHI + ((2 * w + part) * 4 + j) * 1024);
+        for (int j = 0; j < 4; ++j) X.phi[part][j] = ld_frag(r, frag_off, LY.phi + ((2 * w + part) * 4 + j) * 1024);
       } else {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, OFF_Z + ((NT * sg + nt) * 4 + w) * 1024);
+        for (int nt = 0; nt < NT; ++nt) X.z[nt] = ld_frag(r, frag_off, LY.z + ((NT * sg + nt) * 4 + w) * 1024);
       }
     };
     auto load_ops = [&](Ops& X, rsrc_t r) {
+      load_part(X, r, 2);
       load_part(X, r, 0);
       load_part(X, r, 1);
-      load_part(X, r, 2);
     };
     auto chunk_rsrc = [&](int64_t c) {
-      return make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)kBlockBytes);
+      return make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)LY.block);
     };
     // one chunk with operand set X, while set Y (idle since the previous chunk) is loaded with
     // chunk c + 2 (past the end, the last chunk reloads itself), unconditionally and in a
@@ -960,6 +1238,7 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
           *reinterpret_cast<half4*>(&sx[bf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
         }
+      load_part(Y, rn, 2);  // Z first: the next use of a set begins with its Z (the seed)
       load_part(Y, rn, 0);
       __syncthreads();
       // -- this wave's state rows: S = S + Z + Psi S, where Psi S runs as four
@@ -984,9 +1263,8 @@ __global__ __launch_bounds__(512) void rec_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) s[nt][u] = a0[u] + a1[u];
       }
-      load_part(Y, rn, 2);
       // -- the state after every ckpt_chunks full chunks, if asked for
-      if (ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * C <= si.len) {
+      if (CKPT && ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * BL <= si.len) {
         const int64_t slot = ck_base + (c + 1) / ck_every - 1;
         if (slot < ckpt_slots) {
           float* dst = ckpt + (slot * H + h) * DK * DV;
@@ -1025,73 +1303,15 @@ __global__ __launch_bounds__(512) void rec_kernel(
           for (int i = 0; i < 4; ++i)
             S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
     }
-  } else if (job.mode != REC_OUTPUT || (w >> 1) % jobs.halves != half) {
+  } else if (job.mode != REC_OUTPUT || (RT == 4 && jobs.halves == 2 && (w >> 1) != half)) {
     // ------------------------------------------------ no outputs: keep the barriers in step
     for (int64_t c = c_lo; c < c_end; ++c) __syncthreads();
+  } else if (RT == 8 && jobs.halves == 1) {
+    out_waves(IntC<2>{}, w, w + 4);   // every output wave: row tiles w and w + 4
   } else {
-    // ------------------------------------------------ output waves: chunk rows 16w .. 16w+15
-    const int row_stride = H * DV;  // elements between consecutive tokens
-    int o_off[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o_off[nt][i] = ((16 * w + 4 * gq + i) * row_stride + 16 * (NT * sg + nt) + nn) * (int)sizeof(TOut);
-    TOut* o_base = o + (si.tok0 * H + h) * DV;
-    const size_t tok_step = (size_t)C * row_stride;
-    struct Ops {
-      half8 qh[4];
-      floatx4 oh[NT];
-    };
-    Ops A, B;
-    auto load_q = [&](Ops& X, int64_t c) {
-      const rsrc_t r = make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)kBlockBytes);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) X.qh[j] = ld_frag(r, frag_off, OFF_QH + (j * 4 + w) * 1024);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        X.oh[nt] = ld_tile_f16(r, l * 8, OFF_OH + ((NT * sg + nt) * 4 + w) * 512);
-    };
-    auto step = [&](Ops& X, int64_t c) {
-      const int bf = (int)(c & 1);
-      __syncthreads();
-      // the products read the state entering the chunk, from the buffer the state waves
-      // filled before this barrier
-      floatx4 acc[NT], acc2[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = mfma_f16(X.qh[0], state_frag(bf, nt, 0), X.oh[nt]);
-        acc2[nt] = mfma_f16(X.qh[2], state_frag(bf, nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
-        acc[nt] = mfma_f16(X.qh[1], state_frag(bf, nt, 1), acc[nt]);
-        acc2[nt] = mfma_f16(X.qh[3], state_frag(bf, nt, 3), acc2[nt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
-      load_q(X, c + 2);
-      // bytes of the chunk's rows of this head, up to the end of its last valid row
-      const int64_t rows = min((int64_t)C, si.len - c * C);
-      const rsrc_t ro = make_rsrc(o_base + c * tok_step, ((rows - 1) * row_stride + DV) * (int64_t)sizeof(TOut));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (sizeof(TOut) == 4)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[nt][i]), ro, o_off[nt][i], 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[nt][i]), ro, o_off[nt][i], 0, 0);
-        }
-    };
-    if (c_end > c_lo) {
-      load_q(A, c_lo);
-      load_q(B, c_lo + 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // as for the state waves: the loop waits stay partial
-    int64_t c = c_lo;
-    for (; c + 1 < c_end; c += 2) {
-      step(A, c);
-      step(B, c + 1);
-    }
-    if (c < c_end) step(A, c);
+    // one row tile per output wave: tile w (RT = 4, or RT = 8 with each workgroup of a split
+    // pair taking the first or the last four row tiles)
+    out_waves(IntC<1>{}, RT == 8 ? w + 4 * half : w, 0);
   }
 }
 
@@ -1131,16 +1351,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int rr = 0; rr < 8; ++rr) S_next[base + (int64_t)(r0 + rr) * DV + 16 * strip + j] = acc[rr];
 }
 
-int64_t max_chunks(const ChunkPlan& p) {
-  const int64_t per = (p.T + C - 1) / C;
+// Tokens per workspace block and walk step (chosen with the plan): 64, one chunk, or 128, two
+// chunks composed.
+int walk_block(const ChunkPlan& p) { return p.walk_block == 2 * C ? 2 * C : C; }
+
+int64_t max_blocks(const ChunkPlan& p) {
+  const int BL = walk_block(p);
+  const int64_t per = (p.T + BL - 1) / BL;
   return p.cu_seqlens ? per + p.n_seq : (int64_t)p.B * per;
 }
 
-size_t chunk_table_offset(const ChunkPlan& p) {
-  return (size_t)max_chunks(p) * p.H * kBlockBytes;
+size_t block_table_offset(const ChunkPlan& p) {
+  return (size_t)max_blocks(p) * p.H * layout(walk_block(p)).block;
 }
 
-// packed sequences: chunk offsets, then checkpoint offsets, after the blocks
+// packed sequences: block offsets, then checkpoint offsets, then the order, after the blocks
 size_t table_bytes(const ChunkPlan& p) { return ((sizeof(int32_t) * (p.n_seq + 1) + 255) / 256) * 256; }
 
 }  // namespace
@@ -1154,7 +1379,7 @@ namespace {
 int n_segments(const ChunkPlan& p) { return p.segments >= 3 ? p.segments : 1; }
 size_t state_bytes(const ChunkPlan& p) { return (size_t)p.n_seq * p.H * DK * DV * sizeof(float); }
 size_t segment_buffers_offset(const ChunkPlan& p) {
-  return chunk_table_offset(p) + (p.cu_seqlens ? 3 * table_bytes(p) : 0);
+  return block_table_offset(p) + (p.cu_seqlens ? 3 * table_bytes(p) : 0);
 }
 }  // namespace
 
@@ -1165,48 +1390,47 @@ size_t fast_workspace_bytes(const ChunkPlan& p) {
 
 namespace {
 
-template <typename TOut>
+template <typename TOut, int BL>
 hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int halves, int64_t pairs,
-                      RecJobs jobs, int n_jobs, const int32_t* chunk_off,
+                      RecJobs jobs, int n_jobs, const int32_t* blk_off,
                       const int32_t* ckpt_off, const int32_t* order, uint8_t* ws) {
   jobs.halves = halves;
   jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP) * halves;
   const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
-  const int ck_chunks = p.ckpt ? p.ckpt_every / C : 0;
-  auto kern = two ? rec_kernel<TOut, 2> : rec_kernel<TOut, 1>;
+  const int ck_blocks = p.ckpt ? p.ckpt_every / BL : 0;
+  auto kern = p.ckpt ? (two ? rec_kernel<TOut, 2, BL, true> : rec_kernel<TOut, 1, BL, true>)
+                     : (two ? rec_kernel<TOut, 2, BL, false> : rec_kernel<TOut, 1, BL, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, stream, jobs, static_cast<TOut*>(p.o), p.cu_seqlens,
-                     chunk_off, p.T, p.H, p.n_seq, max_chunks(p), ws, p.ckpt, ck_chunks,
+                     blk_off, p.T, p.H, p.n_seq, max_blocks(p), ws, p.ckpt, ck_blocks,
                      p.ckpt_slots, ckpt_off, order);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* chunk_off,
-                       uint8_t* ws, int c_lo, int c_span) {
-  const int64_t blocks = p.cu_seqlens ? max_chunks(p) * p.H : (int64_t)p.n_seq * c_span * p.H;
+template <bool COMPOSE>
+hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* blk_off, uint8_t* ws) {
+  const int64_t blocks = max_blocks(p) * p.H;
+  auto kern = p.pairwise_diag ? prep_kernel<true, COMPOSE> : prep_kernel<false, COMPOSE>;
   if (blocks > 0)
-    hipLaunchKernelGGL(p.pairwise_diag ? prep_kernel<true> : prep_kernel<false>,
-                       dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(COMPOSE ? 512 : 256), 0, stream,
                        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                        static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.g),
-                       static_cast<const uint16_t*>(p.beta), p.cu_seqlens, chunk_off, p.T, p.H,
-                       p.n_seq, ws, c_lo, c_span);
+                       static_cast<const uint16_t*>(p.beta), p.cu_seqlens, blk_off, p.T, p.H,
+                       p.n_seq, ws);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
+template <int BL>
+hipError_t launch_fast(const ChunkPlan& p, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
-  int32_t *chunk_off = nullptr, *ckpt_off = nullptr, *order = nullptr;
+  int32_t *blk_off = nullptr, *ckpt_off = nullptr, *order = nullptr;
   if (p.cu_seqlens) {
-    chunk_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p));
-    ckpt_off = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p) + table_bytes(p));
-    order = reinterpret_cast<int32_t*>(ws + chunk_table_offset(p) + 2 * table_bytes(p));
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seq, p.T,
-                       p.ckpt ? p.ckpt_every : 0, chunk_off, ckpt_off, order);
+    blk_off = reinterpret_cast<int32_t*>(ws + block_table_offset(p));
+    ckpt_off = reinterpret_cast<int32_t*>(ws + block_table_offset(p) + table_bytes(p));
+    order = reinterpret_cast<int32_t*>(ws + block_table_offset(p) + 2 * table_bytes(p));
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seq, p.T, BL,
+                       p.ckpt ? p.ckpt_every : 0, blk_off, ckpt_off, order);
   }
   const int64_t pairs = (int64_t)p.n_seq * p.H;
-  const int ncs = (int)((p.T + C - 1) / C);
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1216,28 +1440,28 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
   // measured faster from one strip per CU on (prefill-64k-bound -1.5 %).
   const WalkShape shape = walk_shape(pairs, n_cu, p.S0 != nullptr && p.S0 == p.S_T);
   const bool two = shape.two_strips;
-  hipError_t e = launch_prep(p, stream, chunk_off, ws, 0, ncs);
+  hipError_t e = launch_prep<BL == 2 * C>(p, stream, blk_off, ws);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
-    return p.out_bf16 ? launch_rec<uint16_t>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, order, ws)
-                      : launch_rec<float>(p, stream, two, halves, pairs, jobs, n_jobs, chunk_off, ckpt_off, order, ws);
+    return p.out_bf16 ? launch_rec<uint16_t, BL>(p, stream, two, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws)
+                      : launch_rec<float, BL>(p, stream, two, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws);
   };
   RecJobs jobs = {};
   const int P = n_segments(p);
-  if (P == 1) {  // one walk over every chunk
+  if (P == 1) {  // one walk over every block
     jobs.job[0] = RecJob{0, INT64_MAX, p.S0, p.S_T, REC_OUTPUT};
-    // The walk is bound by each CU's vector memory unit (the operand bytes per chunk). When
+    // The walk is bound by each CU's vector memory unit (the operand bytes per step). When
     // the walks would leave at least half of the CUs idle, two workgroups per walk run the
     // same state walk and split the output rows, so each loads the state operands and half of
     // the output operands (never in place: see walk_shape).
     return rec(jobs, 1, shape.halves);
   }
-  // Segmented walk (sequence split of the transition form): the chunks of each sequence are
+  // Segmented walk (sequence split of the transition form): the blocks of each sequence are
   // cut at b_1 < ... < b_{P-1}. Pass 1 walks segment 0 from S0 (its exit is segment 1's entry)
   // and, at the same time, every middle segment p from zeros (Z_p) and from the identity with
   // V = 0 (Phi_p). Then entry_{p+1} = Phi_p entry_p + Z_p, in order. Pass 2 walks segments
   // 1 .. P-1 from their entries, all at once.
-  const int64_t span = ((p.T + C - 1) / C + P - 1) / P;  // chunks per segment (T bounds any sequence)
+  const int64_t span = ((p.T + BL - 1) / BL + P - 1) / P;  // blocks per segment (T bounds any sequence)
   float* buf = reinterpret_cast<float*>(ws + segment_buffers_offset(p));
   const size_t ns = state_bytes(p) / sizeof(float);
   auto entry = [&](int q) { return buf + (size_t)(q - 1) * ns; };                   // q = 1 .. P-1
@@ -1260,6 +1484,12 @@ hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
     jobs.job[n++] = RecJob{q * span, q == P - 1 ? INT64_MAX : (q + 1) * span, entry(q),
                            q == P - 1 ? p.S_T : nullptr, REC_OUTPUT};
   return rec(jobs, n, 1);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fast(const ChunkPlan& p, hipStream_t stream) {
+  return walk_block(p) == 2 * C ? launch_fast<2 * C>(p, stream) : launch_fast<C>(p, stream);
 }
 
 }  // namespace kda

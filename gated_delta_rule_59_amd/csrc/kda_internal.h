@@ -32,6 +32,8 @@ struct ChunkPlan {
   int ckpt_slots;
   bool pairwise_diag;  // matrix-core path: diagonal tiles pairwise (no decay bound needed)
   int segments;        // matrix-core path: walk each sequence in this many segments (>= 3), else 1
+  int walk_block;      // matrix-core path: tokens per walk step, 64 (one chunk) or 128 (two
+                       // chunks composed into one step)
 };
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);

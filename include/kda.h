@@ -109,6 +109,16 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *              that the decay bound makes possible (orkas.ai Kimi K3 page, "Eine Untergrenze, die
  *              einen GPU-Codepfad beseitigte"). It needs no lower bound on g (any g <= 0) and is
  *              slower: the ablation of that bound. (KDA_CHECK=1 still checks g >= -5.)
+ *              KDA_FLAG_WALK64 / KDA_FLAG_WALK128 to make the matrix-core path's serial walk
+ *              over the chunks take one 64-token chunk per step, or two consecutive chunks
+ *              composed into one 128-token step (S -> S + Z + Psi S for the pair, formed in
+ *              parallel beforehand). Performance knobs (results agree to rounding): composing
+ *              halves the serial steps and the workspace bytes per token, at about 30 % more
+ *              parallel work. Without either flag the library composes when there are at most
+ *              8 (sequence, head) pairs (where the serial walk dominates). One chunk per step is
+ *              always taken when ckpt_every is not a multiple of 128, since checkpoints are
+ *              taken between steps (KDA_FLAG_WALK128 is then refused); the workspace size
+ *              depends on ckpt_every, so query it with the same value.
  *   ckpt, ckpt_every, ckpt_slots
  *              Sparse state checkpoints for prefix reuse: the fixed-size state is the whole
  *              memory of a prefix, so a later request that shares the prefix can resume from
@@ -155,6 +165,8 @@ typedef struct {
 
 #define KDA_FLAG_GENERIC 1u
 #define KDA_FLAG_PAIRWISE_DIAG 2u
+#define KDA_FLAG_WALK64 4u
+#define KDA_FLAG_WALK128 8u
 
 /* Arguments of kda_decode_step: one token for each of N independent sequences.
  *   q, k, g [N, H, dk];  v [N, H, dv];  beta [N, H]   (act_dtype / gate_dtype as above)
@@ -195,7 +207,9 @@ typedef struct {
 /* Bytes of device workspace kda_chunk_fwd needs for these arguments (pointers are not
  * inspected); 0 when the chosen path needs none. Validates shapes and dtypes like
  * kda_chunk_fwd and returns SIZE_MAX (with kda_last_error() set) when they are invalid.
- * The matrix-core path needs one 98,304-byte block per (chunk, head) plus small tables. */
+ * The matrix-core path needs one 114,688-byte block per 64-token chunk and head when it walks
+ * one chunk per step, or one 163,840-byte block per 128 tokens (two chunks) and head when it
+ * composes two per step, plus small tables. */
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_args* args);
 
 /* Prefill: o and S_T from q, k, v, g, beta and S0, enqueued on hip_stream (hipStream_t). */
@@ -208,7 +222,8 @@ kda_status kda_chunk_fwd(const kda_chunk_args* args, void* hip_stream);
  * That scratch is a static array of the library, held by every GPU the library runs on from
  * the first use there until the process ends. Calls whose kda_chunk_fwd_workspace_bytes()
  * exceeds KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything is enqueued (at
- * most 1,365 (chunk, head) pairs of 64 tokens, e.g. 4,096 tokens with 16 heads). No device
+ * most 1,170 (64-token chunk, head) pairs with one chunk per walk step, or 819 (128-token
+ * block, head) pairs with composed steps; prefill-4k, 4,096 tokens with 16 heads, fits). No device
  * or host memory is allocated. All calls on one GPU share its scratch, whatever their stream:
  * calls that overlap in time on one GPU race (serialise them, e.g. on one stream). */
 #define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)

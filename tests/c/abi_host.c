@@ -42,11 +42,11 @@ int main(void) {
          KDA_ABI_VERSION);
   EXPECT(strcmp(kda_status_string(KDA_ERR_ALIAS), "KDA_ERR_ALIAS") == 0, "status string");
 
-  /* workspace: the matrix-core path needs one 98,304-byte block per (chunk, head) */
+  /* workspace: 4 heads (composed steps): one 163,840-byte block per 128 tokens and head */
   kda_chunk_args a = base_args();
   size_t bytes = kda_chunk_fwd_workspace_bytes(&a);
   EXPECT(bytes != SIZE_MAX, "workspace query: %s", kda_last_error());
-  EXPECT(bytes >= (size_t)4 * 4 * 98304, "workspace %zu bytes", bytes);
+  EXPECT(bytes >= (size_t)2 * 4 * 163840, "workspace %zu bytes", bytes);
   a.flags = KDA_FLAG_GENERIC;
   bytes = kda_chunk_fwd_workspace_bytes(&a);
   EXPECT(bytes == 0, "fp32 path workspace %zu", bytes);

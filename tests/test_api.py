@@ -67,12 +67,29 @@ def call_chunk(b, a):
 
 @pytest.mark.parametrize("field,value,status", [
     ("dk", 96, 2), ("dv", 256, 2), ("chunk", 48, 2), ("B", 0, 2), ("T", -1, 2), ("H", 0, 2),
-    ("act_dtype", 7, 3), ("gate_dtype", 0, 3), ("flags", 8, 4), ("flags", 4, 4), ("segments", 9, 2), ("segments", -1, 2),
+    ("act_dtype", 7, 3), ("gate_dtype", 0, 3), ("flags", 16, 4), ("flags", 32, 4), ("segments", 9, 2), ("segments", -1, 2),
 ])
 def test_chunk_rejects_bad_shapes_and_dtypes(b, field, value, status):
     rc, msg = call_chunk(b, base_args(b, **{field: value}))
     assert rc == status, msg
     assert msg
+
+
+def test_walk_step_flags(b):
+    """KDA_FLAG_WALK64 and KDA_FLAG_WALK128 exclude each other; 128-token steps cannot take
+    checkpoints that fall between them. Without a flag, few (sequence, head) pairs compose two
+    chunks per step (one 163,840-byte block per 128 tokens and head) and many take one (114,688
+    bytes per 64-token chunk and head)."""
+    rc, msg = call_chunk(b, base_args(b, flags=b.KDA_FLAG_WALK64 | b.KDA_FLAG_WALK128))
+    assert rc == 4 and "exclude" in msg
+    a = base_args(b, flags=b.KDA_FLAG_WALK128, ckpt=FAKE + (1 << 33), ckpt_every=64, ckpt_slots=4)
+    rc, msg = call_chunk(b, a)
+    assert rc == 4 and "between" in msg
+    q = lambda a: b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a))  # noqa: E731
+    assert q(base_args(b, H=8)) == 2 * 8 * 163840                  # 8 pairs: composed
+    assert q(base_args(b, H=9)) == 4 * 9 * 114688                  # 9 pairs: one chunk per step
+    assert q(base_args(b, H=9, flags=b.KDA_FLAG_WALK128)) == 2 * 9 * 163840
+    assert q(base_args(b, H=8, flags=b.KDA_FLAG_WALK64)) == 4 * 8 * 114688
 
 
 def test_chunk_rejects_null_and_alias(b):
@@ -114,8 +131,10 @@ def test_chunk_checkpoint_rules(b):
 def test_workspace_query(b):
     q = lambda a: b.lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(a))  # noqa: E731
     fast = q(base_args(b))
-    # one 98,304-byte block per (chunk, head): 4 chunks of 64 tokens, 4 heads
-    assert fast >= 4 * 4 * 98304
+    # 4 heads compose two chunks per step: one 163,840-byte block per 128 tokens and head;
+    # 114,688 bytes per 64-token chunk and head when the walk takes one chunk per step
+    assert fast >= 2 * 4 * 163840
+    assert q(base_args(b, flags=b.KDA_FLAG_WALK64)) >= 4 * 4 * 114688
     assert q(base_args(b, flags=b.KDA_FLAG_GENERIC)) == 0
     assert q(base_args(b, act_dtype=b.KDA_F32, gate_dtype=b.KDA_F32)) == 0
     assert q(base_args(b, dk=96)) == b.SIZE_MAX and b.lib().kda_last_error()
@@ -126,10 +145,10 @@ def test_workspace_query(b):
 
 def test_noalloc_refuses_sizes_beyond_its_scratch(b):
     """kda_chunk_fwd_noalloc checks its sizes against the fixed scratch before touching a
-    device: 1,366 (chunk, head) blocks of 98,304 B exceed KDA_NOALLOC_SCRATCH_BYTES."""
+    device: 820 (128-token block, head) pairs of 163,840 B exceed KDA_NOALLOC_SCRATCH_BYTES."""
     assert b.NOALLOC_SCRATCH_BYTES == 128 << 20
-    a = base_args(b, T=64 * 1366, H=1)
-    tok = 64 * 1366
+    a = base_args(b, T=128 * 820, H=1)
+    tok = 128 * 820
     a.k, a.v, a.g, a.beta = (FAKE + i * tok * 128 * 2 for i in range(1, 5))
     a.o = FAKE + (1 << 34)
     rc = b.lib().kda_chunk_fwd_noalloc(ctypes.byref(a), None)

@@ -70,7 +70,10 @@ def test_checkpoints_match_prefix_states(case, every, generic):
     q, k, v, g, beta, S0, cu = kda_inputs_dev(x)
     ck = torch.full((slots + 1, x.wl.H, 128, 128), float("nan"), device="cuda")  # one spare
     o, s = binding.chunk_fwd(q, k, v, g, beta, S0, cu, generic=generic, ckpt=ck, ckpt_every=every)
-    o_plain, s_plain = binding.chunk_fwd(q, k, v, g, beta, S0, cu, generic=generic)
+    # the plain call takes the same walk steps: checkpoints between 128-token steps make the
+    # matrix-core walk take one chunk per step, as walk64 does
+    o_plain, s_plain = binding.chunk_fwd(q, k, v, g, beta, S0, cu, generic=generic,
+                                         walk64=every % 128 != 0)
     torch.cuda.synchronize()
     want = expected_checkpoints(x, every)
     assert want.shape[0] == slots > 0

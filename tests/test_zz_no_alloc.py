@@ -26,7 +26,7 @@ def _both(x, **kw):
 
 def test_noalloc_matches_chunk_fwd_twice_then_smaller():
     import torch
-    cases = [("prefill-4k full size (1,024 chunk-head blocks, 117 MB of scratch)",
+    cases = [("prefill-4k full size (1,024 chunk-head blocks, 112 MiB of scratch)",
               inputs.make_prefill(1), {}),
              ("T=300 H=2, a smaller input after a larger one", inputs.make_prefill(1, T=300, H=2), {})]
     for label, x, kw in cases:
@@ -59,7 +59,7 @@ def test_noalloc_rejects_more_than_its_scratch():
     output left untouched."""
     import torch
     from gated_delta_rule_59_amd import binding
-    B, T, H = 1, 64 * 1366, 1   # 1,366 chunk-head blocks of 98,304 B > 128 MiB
+    B, T, H = 1, 128 * 820, 1   # 820 blocks of 163,840 B > 128 MiB
     q = torch.zeros((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
     beta = torch.zeros((B, T, H), dtype=torch.bfloat16, device="cuda")
     o = torch.full((B, T, H, 128), 7.0, dtype=torch.float32, device="cuda")
