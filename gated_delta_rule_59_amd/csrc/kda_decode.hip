@@ -14,6 +14,8 @@
 // (CG = DV / 4 column groups, one 16-byte vector) and key rows (t / CG) + RG * i,
 // i < DK / RG (RG = 256 / CG row groups), so every wave reads whole 512-byte rows and the
 // state stays in registers between the read and the write.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -109,7 +111,9 @@ __global__ __launch_bounds__(256, 7) void decode_step_kernel(
 // when o is given. With accept == nullptr the state is left as it was (verification); with
 // accept, S[n] becomes the state after the first clamp(accept[n], 0, m) tokens. The state
 // stays in registers across the tokens: one read of S, and one write only when committing.
-// Same thread layout as decode_step_kernel; inputs are [N, m, H, d].
+// Same thread layout as decode_step_kernel; inputs are [N, m, H, d]. This token loop serves a
+// single draft, more than eight, and head sizes other than 128; draft_chunk_kernel below
+// takes 2..8 drafts at dk = dv = 128 in one pass.
 // At least 4 waves per SIMD (128 VGPRs): verification of 4 drafts on the 1 GiB decode state
 // takes 0.264 ms against 0.296 ms at the 140 VGPRs the compiler picks unconstrained.
 template <int DK, int DV, typename TIn, typename TOut>
@@ -201,14 +205,253 @@ __global__ __launch_bounds__(256, 4) void decode_multi_kernel(
   }
 }
 
+// Several drafts as one mini-chunk of the chunked form (the same algebra the prefill uses for
+// its 64-token chunks). For tokens i < m of (n, h) entering with state S, per key channel c:
+//   d_i = e^{g_i},  Gam_i = d_0 ... d_i,  P(l, i) = d_{l+1} ... d_i  (P(i, i) = 1)
+//   state before token i's write:  Diag(Gam_i) S + sum_{l<i} Diag(P(l, i)) b_l k_l u_l^T, so
+//   u_i = v_i - S^T (Gam_i k_i) - sum_{l<i} A_il u_l,   A_il = b_l sum_c k_ic k_lc P(l, i)_c
+//   o_j = S^T (Gam_j q_j) + sum_{i<=j} B_ji u_i,          B_ji = b_i sum_c q_jc k_ic P(i, j)_c
+//   state after the first a tokens:  Diag(Gam_{a-1}) S + sum_{l<a} Diag(P(l, a-1)) b_l k_l u_l^T
+// The state enters only through the 2m column reductions S^T (Gam_i k_i) and S^T (Gam_j q_j):
+// one pass over S serves every draft, a verification streams S through 2m accumulators per
+// column and holds none of it, and a commit keeps its slice of S in registers for the one
+// update with all accepted tokens. M >= m is the register size (missing tokens are zero).
+//
+// Thread t of wave w owns value columns 2 (t & 63), +1 and key rows w + 4 i (i < 32): every
+// load is one 512-byte row per wave, and the column partial sums of a wave need no exchange
+// between its lanes. Verification and commit share every instruction that forms the outputs,
+// written as explicit fused multiply-adds in a fixed order, so a commit call writes outputs
+// bitwise equal to those of the verification call with the same inputs.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Sum over the 16 lanes of a DPP row, left in the row's last lane (inclusive scan, zero fill).
+__device__ __forceinline__ float dpp_row_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  return x;
+}
+
+// Occupancy (waves per SIMD) on the 1 GiB decode state with four drafts: a verification at 6
+// (72 VGPRs; 0.187 ms, against 0.187 at 7 and 0.189 at 8), a commit at 4 (the 128 x 128
+// state held in 64 VGPRs; 0.381 ms, against 0.390 at 5). Eight drafts fit 3 workgroups per CU
+// in LDS.
+template <int M, bool COMMIT, bool OUT, typename TIn, typename TOut>
+__global__ __launch_bounds__(256, M > 4 ? 3 : (COMMIT ? 4 : 6)) void draft_chunk_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ S,
+    TOut* __restrict__ o, const int32_t* __restrict__ accept, int H, int m,
+    int64_t n_heads_total) {
+  constexpr int DK = 128, DV = 128;
+  constexpr int RPT = DK / 4;  // rows per thread
+  constexpr int WIN = 8;       // rows in flight per thread while verifying
+  constexpr int NAB = M * M;   // A_il at [i][l] (l < i), B_ji at [i][j] (i <= j)
+  constexpr int NT = OUT ? 2 * M : M;  // reductions: S^T (Gam_i k_i), then S^T (Gam_j q_j)
+  static_assert(M % 4 == 0 && RPT % WIN == 0 && (COMMIT || OUT), "shape");
+
+  const int64_t nh = blockIdx.x;  // (n * H + h)
+  if (nh >= n_heads_total) return;
+  const int64_t n = nh / H, h = nh % H;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int a = COMMIT ? min(max(accept[n], 0), m) : 0;  // tokens committed to S
+
+  __shared__ __align__(16) float s_tab[DK][NT];      // row c: Gam_i k_ic (i < M), Gam_j q_jc
+  __shared__ __align__(16) float s_red[4][NT][DV];   // per-wave column sums
+  __shared__ float s_part[8][NAB];                      // 16-channel partial sums of A, B
+  __shared__ float s_ab[NAB];
+  __shared__ __align__(16) float s_cf[COMMIT ? DK : 1][M];  // b_l k_lc P(l, a-1)_c, l < a
+  __shared__ float s_gam[COMMIT ? DK : 1];                  // Gam_{a-1}
+  __shared__ __align__(16) float s_u[COMMIT ? M : 1][DV];
+
+  // ---- the drafts' inputs first (threads 0..127 own key channel c = t, and value column t):
+  //      loads complete in issue order, so the work on them below waits for these loads only,
+  //      not for the state behind them
+  float kk[M], qq[M], dd[M], bb[M], vv[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) kk[i] = qq[i] = dd[i] = bb[i] = vv[i] = 0.f;
+  if (t < DK) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (i < m) {
+        const int64_t tok = (n * m + i) * H + h;
+        kk[i] = ld(k, tok * DK + t);
+        qq[i] = ld(q, tok * DK + t);
+        dd[i] = ld(g, tok * DK + t);
+        bb[i] = ld(beta, tok);
+        vv[i] = ld(v, tok * DV + t);
+      }
+    }
+  }
+  const floatx2* Sv = reinterpret_cast<const floatx2*>(S + nh * (int64_t)DK * DV);
+  auto s_ptr = [&](int i) { return &Sv[(w + 4 * i) * (DV / 2) + lane]; };
+  floatx2 s[COMMIT ? RPT : WIN];
+#pragma unroll
+  for (int i = 0; i < (COMMIT ? RPT : WIN); ++i) s[i] = __builtin_nontemporal_load(s_ptr(i));
+
+  // ---- per key channel (threads 0..127): decay products, the reduction tables, the terms
+  //      of A and B, and (commit) the update coefficients
+  if (t < DK) {
+    const int c = t;
+#pragma unroll
+    for (int i = 0; i < M; ++i) dd[i] = i < m ? __expf(dd[i]) : 1.f;  // e^{g_i}; 1 past the drafts
+    float tk[M], tq[M];
+    float gam = 1.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      gam = gam * dd[i];
+      tk[i] = gam * kk[i];
+      tq[i] = gam * qq[i];
+      if (COMMIT && i == a - 1) s_gam[c] = gam;
+    }
+#pragma unroll
+    for (int i = 0; i < M; i += 4) {
+      *reinterpret_cast<floatx4*>(&s_tab[c][i]) = floatx4{tk[i], tk[i + 1], tk[i + 2], tk[i + 3]};
+      if (OUT)
+        *reinterpret_cast<floatx4*>(&s_tab[c][M + i]) = floatx4{tq[i], tq[i + 1], tq[i + 2], tq[i + 3]};
+    }
+    // terms: pair (l, i), l <= i, with P = P(l, i)
+    float cf[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) cf[i] = 0.f;
+#pragma unroll
+    for (int l = 0; l < M; ++l) {
+      float P = 1.f;
+#pragma unroll
+      for (int i = l; i < M; ++i) {
+        if (i > l) P = P * dd[i];
+        if (COMMIT && i == a - 1) cf[l] = (bb[l] * kk[l]) * P;
+        const float kp = kk[l] * P;
+        float ta = 0.f, tb = 0.f;
+        if (i > l) ta = dpp_row_sum(kk[i] * kp);  // A_il / b_l
+        if (OUT) tb = dpp_row_sum(qq[i] * kp);     // B_il / b_l (token i's output, draft l)
+        if ((lane & 15) == 15) {
+          if (i > l) s_part[4 * w + (lane >> 4)][i * M + l] = ta;
+          if (OUT) s_part[4 * w + (lane >> 4)][l * M + i] = tb;
+        }
+      }
+    }
+    if (COMMIT) {
+#pragma unroll
+      for (int i = 0; i < M; i += 4)
+        *reinterpret_cast<floatx4*>(&s_cf[c][i]) = floatx4{cf[i], cf[i + 1], cf[i + 2], cf[i + 3]};
+    }
+  }
+  __syncthreads();
+  if (t < NAB && (OUT || t % M < t / M)) {  // (r, c): A_rc = b_c sum (c < r), B_cr = b_r sum (r <= c)
+    const int r = t / M, cc = t % M;
+    float sum = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) sum += s_part[p][t];
+    const int bi = cc < r ? cc : r;  // the draft whose b scales the entry (0 past the drafts)
+    float b = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) b = i == bi ? bb[i] : b;
+    s_ab[t] = sum * b;
+  }
+
+  // ---- one pass over S: the 2M column reductions of this thread's rows
+  floatx2 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = floatx2{0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const floatx2 x = s[COMMIT ? i : i % WIN];
+    if (!COMMIT && i + WIN < RPT) s[i % WIN] = __builtin_nontemporal_load(s_ptr(i + WIN));
+    const float* tr = s_tab[w + 4 * i];
+#pragma unroll
+    for (int j = 0; j < NT; j += 4) {
+      const floatx4 f = *reinterpret_cast<const floatx4*>(tr + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[j + e].x = fmaf(x.x, f[e], acc[j + e].x);
+        acc[j + e].y = fmaf(x.y, f[e], acc[j + e].y);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) *reinterpret_cast<floatx2*>(&s_red[w][j][2 * lane]) = acc[j];
+  __syncthreads();
+
+  // ---- per value column (threads 0..127): the triangular solve for u, then the outputs
+  if (t < DV) {
+    const int c = t;
+    float u[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const float rk = ((s_red[0][i][c] + s_red[1][i][c]) + s_red[2][i][c]) + s_red[3][i][c];
+      float x = vv[i] - rk;
+#pragma unroll
+      for (int l = 0; l < i; ++l) x = fmaf(-s_ab[i * M + l], u[l], x);
+      u[i] = x;
+      if (COMMIT) s_u[i][c] = x;
+    }
+    if (OUT) {
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        if (j >= m) break;
+        float y = ((s_red[0][M + j][c] + s_red[1][M + j][c]) + s_red[2][M + j][c]) + s_red[3][M + j][c];
+#pragma unroll
+        for (int i = 0; i <= j; ++i) y = fmaf(s_ab[i * M + j], u[i], y);
+        st(o, ((n * m + j) * H + h) * DV + c, y);
+      }
+    }
+  }
+  if constexpr (COMMIT) {
+    __syncthreads();
+    if (a > 0) {
+      // rejected drafts get u = 0 as well as a zero coefficient, so that whatever their
+      // inputs hold adds nothing
+      floatx2 ul[M];
+#pragma unroll
+      for (int l = 0; l < M; ++l)
+        ul[l] = l < a ? *reinterpret_cast<const floatx2*>(&s_u[l][2 * lane]) : floatx2{0.f, 0.f};
+      floatx2* Sw = reinterpret_cast<floatx2*>(S + nh * (int64_t)DK * DV);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = w + 4 * i;
+        const float gm = s_gam[r];
+        floatx2 x = {s[i].x * gm, s[i].y * gm};
+#pragma unroll
+        for (int l = 0; l < M; l += 4) {
+          const floatx4 cl = *reinterpret_cast<const floatx4*>(&s_cf[r][l]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x.x = fmaf(cl[e], ul[l + e].x, x.x);
+            x.y = fmaf(cl[e], ul[l + e].y, x.y);
+          }
+        }
+        __builtin_nontemporal_store(x, &Sw[r * (DV / 2) + lane]);
+      }
+    }
+  }
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_decode_multi_t(const DecodeMultiPlan& p, hipStream_t stream) {
   const int64_t nh = (int64_t)p.N * p.H;
+  const TIn *q = static_cast<const TIn*>(p.q), *k = static_cast<const TIn*>(p.k),
+            *v = static_cast<const TIn*>(p.v), *g = static_cast<const TIn*>(p.g),
+            *beta = static_cast<const TIn*>(p.beta);
+  TOut* o = static_cast<TOut*>(p.o);
+  if constexpr (DK == 128 && DV == 128) {
+    // 2..8 drafts: one pass over S (a single token, and longer drafts, take the token loop)
+    if (p.m >= 2 && p.m <= 8) {
+      auto pick = [&](auto M) {
+        constexpr int Mv = decltype(M)::value;
+        return !p.accept ? draft_chunk_kernel<Mv, false, true, TIn, TOut>
+               : o       ? draft_chunk_kernel<Mv, true, true, TIn, TOut>
+                         : draft_chunk_kernel<Mv, true, false, TIn, TOut>;
+      };
+      auto kern = p.m <= 4 ? pick(std::integral_constant<int, 4>{})
+                           : pick(std::integral_constant<int, 8>{});
+      hipLaunchKernelGGL(kern, dim3((unsigned)nh), dim3(256), 0, stream, q, k, v, g, beta, p.S, o,
+                         p.accept, p.H, p.m, nh);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((decode_multi_kernel<DK, DV, TIn, TOut>), dim3((unsigned)nh), dim3(256), 0,
-                     stream, static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
-                     static_cast<const TIn*>(p.v), static_cast<const TIn*>(p.g),
-                     static_cast<const TIn*>(p.beta), p.S, static_cast<TOut*>(p.o), p.accept,
-                     p.H, p.m, nh);
+                     stream, q, k, v, g, beta, p.S, o, p.accept, p.H, p.m, nh);
   return hipGetLastError();
 }
 

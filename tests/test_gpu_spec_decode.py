@@ -29,8 +29,12 @@ def oracle_after(q, k, v, g, beta, S, accept):
     return s
 
 
+# d = 128 with 2..8 drafts takes the one-pass kernel (register sizes 4 and 8, padded when m is
+# smaller); one draft, more than eight, and other head sizes take the token loop
 @pytest.mark.parametrize("N,H,m,d,dtype", [(48, 4, 5, 128, "bf16"), (8, 2, 3, 64, "bf16"),
-                                           (6, 2, 4, 32, "f32")])
+                                           (6, 2, 4, 32, "f32"), (32, 4, 2, 128, "bf16"),
+                                           (20, 3, 4, 128, "bf16"), (16, 2, 8, 128, "f32"),
+                                           (12, 2, 3, 128, "f32"), (8, 2, 9, 128, "bf16")])
 def test_verify_then_commit(N, H, m, d, dtype):
     import torch
     from gated_delta_rule_59_amd import binding
