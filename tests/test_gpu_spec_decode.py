@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from gated_delta_rule_59_amd import inputs
-from tests.gpu_util import TAU, assert_parity, dev, host
+from tests.gpu_util import TAU, assert_parity, dev, host, rms
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +106,29 @@ def test_spec_decode_workload_size():
     assert_parity(host(o), o_ref, TAU["bf16"], "decode-512 draft outputs")
     assert_parity(host(tS), oracle_after(q, k, v, g, beta, S, acc), TAU["bf16"],
                   "decode-512 committed states")
+
+
+@pytest.mark.parametrize("m", [2, 4, 7])
+def test_bf16_outputs_and_accept_clamped(m):
+    """bf16 outputs (within half a bf16 ulp of the oracle plus the bar) from verify and commit,
+    bitwise equal to each other; accept values below 0 or above m act as 0 and m."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    N, H, d = 24, 2, 128
+    print(f"spec decode bf16 out, clamped accept: m={m}", flush=True)
+    q, k, v, g, beta, S = draft_case(N, H, m, d, "bf16", (24, m))
+    tq, tk, tv, tg, tb = (dev(a, "bf16") for a in (q, k, v, g, beta))
+    tS = torch.from_numpy(S).cuda()
+    o_v = binding.decode_multi(tq, tk, tv, tg, tb, tS, out_dtype=torch.bfloat16)
+    acc = np.random.default_rng([24, m]).integers(-2, m + 3, size=N).astype(np.int32)
+    acc[:4] = [-5, 0, m, m + 7]
+    o_c = binding.decode_multi(tq, tk, tv, tg, tb, tS, accept=torch.from_numpy(acc).cuda(),
+                               out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_v)
+    o_ref, _ = oracle.kda_reference(q, k, v, g, beta, S)
+    bound = 2.0 ** -8 * np.abs(o_ref) + TAU["bf16"] * rms(o_ref)
+    assert (np.abs(host(o_v) - o_ref) <= bound).all()
+    kept = np.clip(acc, 0, m)
+    assert_parity(host(tS), oracle_after(q, k, v, g, beta, S, kept), TAU["bf16"],
+                  "committed states, clamped accept")
