@@ -41,6 +41,12 @@
 //    splitting the value columns over workgroups is exact. When the walks would leave half of
 //    the CUs idle, two workgroups repeat each walk and split its output rows; packed
 //    sequences are walked longest first.
+// With few (sequence, head) pairs the walk's serial latency dominates, and one step of the
+// walk covers two chunks a, b: a prep workgroup of eight waves forms both chunks (four waves
+// each) and composes them, S -> S + Z' + Psi' S with Psi' = Psi_a + Psi_b + Psi_b Psi_a and
+// Z' = Z_a + Z_b + Psi_b Z_a, chunk b's outputs reading the state entering the pair through
+// Qhat_b (I + Psi_a) and Ohat_b + Qhat_b Z_a. Half the steps, and Psi' and Z' stored once
+// per 128 tokens.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_plan.h"
