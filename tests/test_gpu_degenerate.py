@@ -8,7 +8,8 @@ forms the recurrence reduces to:
     and any g (the decayed state's prediction of v_t is replaced by v_t itself);
   - g = -5 on every key channel: every 16-token tile's cumulative log-decay is exactly -80,
     the edge of the range the decay bound guarantees.
-Both prefill paths (the matrix-core path and the fp32 path) and the decode step are covered."""
+Both prefill paths (the matrix-core path and the fp32 path), the decode step and speculative
+drafts are covered."""
 import numpy as np
 import pytest
 
@@ -157,3 +158,40 @@ def test_decode_degenerate_gates():
     o_ref, s_ref = oracle.kda_decode_reference(q, ku, v, g, np.ones_like(beta), S)
     assert_parity(host(o), o_ref, TAU["bf16"], "decode beta=1 o")
     assert_parity(host(Sd), s_ref, TAU["bf16"], "decode beta=1 S")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_drafts_degenerate_gates(m):
+    """Speculative drafts (one-pass kernel for m = 2..8, token loop for m = 1): beta = 0 and
+    g = 0 make every draft's output S^T q_j and a commit of all drafts leave S bitwise
+    unchanged; beta = 1 with unit keys makes the committed state predict the last draft's v
+    exactly (S_new^T k = v)."""
+    import torch
+    from gated_delta_rule_59_amd import binding
+    N, Hd, d = 8, 2, 128
+    print(f"draft degenerate gates: m={m}", flush=True)
+    q, k, v, g, beta = inputs.draw_activations((41, m), N, m, Hd, d, d, "bf16")
+    S = inputs.draw_state((41, m), N, Hd, d, d)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
+    all_in = torch.full((N,), m, dtype=torch.int32, device="cuda")
+
+    Sd = torch.from_numpy(S).cuda()
+    o = binding.decode_multi(dv(q), dv(k), dv(v), dv(np.zeros_like(g)), dv(np.zeros_like(beta)),
+                             Sd, accept=all_in)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(Sd), S)
+    o_ref = np.einsum("nmhc,nhcv->nmhv", q.astype(np.float64), S.astype(np.float64))
+    assert_parity(host(o), o_ref, TAU["bf16"], "drafts beta=0 g=0 o vs S^T q")
+
+    rng = np.random.default_rng([0, 7, 100 + m])
+    ku = np.zeros_like(k)
+    for idx in np.ndindex(N, m, Hd):
+        ch = rng.choice(d, 64, replace=False)
+        ku[idx + (ch,)] = rng.choice([-0.125, 0.125], 64)
+    Sd = torch.from_numpy(S).cuda()
+    binding.decode_multi(dv(q), dv(ku), dv(v), dv(g), dv(np.ones_like(beta)), Sd, accept=all_in,
+                         want_output=False)
+    torch.cuda.synchronize()
+    Sn = host(Sd).astype(np.float64)
+    pred = np.einsum("nhcv,nhc->nhv", Sn, ku[:, -1].astype(np.float64))
+    assert_parity(pred, v[:, -1].astype(np.float64), TAU["bf16"], "drafts beta=1 S_new^T k_last vs v_last")
