@@ -1399,15 +1399,19 @@ size_t fast_workspace_bytes(const ChunkPlan& p) {
 namespace {
 
 template <typename TOut, int BL>
-hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, bool two, int halves, int64_t pairs,
+hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, int strips, int halves, int64_t pairs,
                       RecJobs jobs, int n_jobs, const int32_t* blk_off,
                       const int32_t* ckpt_off, const int32_t* order, uint8_t* ws) {
   jobs.halves = halves;
-  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (two ? NSTRIP / 2 : NSTRIP) * halves;
+  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (NSTRIP / strips) * halves;
   const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
   const int ck_blocks = p.ckpt ? p.ckpt_every / BL : 0;
-  auto kern = p.ckpt ? (two ? rec_kernel<TOut, 2, BL, true> : rec_kernel<TOut, 1, BL, true>)
-                     : (two ? rec_kernel<TOut, 2, BL, false> : rec_kernel<TOut, 1, BL, false>);
+  auto kern = p.ckpt ? (strips == 4   ? rec_kernel<TOut, 4, BL, true>
+                        : strips == 2 ? rec_kernel<TOut, 2, BL, true>
+                                      : rec_kernel<TOut, 1, BL, true>)
+                     : (strips == 4   ? rec_kernel<TOut, 4, BL, false>
+                        : strips == 2 ? rec_kernel<TOut, 2, BL, false>
+                                      : rec_kernel<TOut, 1, BL, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, stream, jobs, static_cast<TOut*>(p.o), p.cu_seqlens,
                      blk_off, p.T, p.H, p.n_seq, max_blocks(p), ws, p.ckpt, ck_blocks,
                      p.ckpt_slots, ckpt_off, order);
@@ -1445,14 +1449,15 @@ hipError_t launch_fast(const ChunkPlan& p, hipStream_t stream) {
   // Few (sequence, head) pairs: the chunk walk is latency bound, so one 16-column strip per
   // workgroup maximises parallelism. At least one strip per CU: two strips per workgroup halve
   // the state operand traffic per column (the walk is bound by each CU's vector memory unit);
-  // measured faster from one strip per CU on (prefill-64k-bound -1.5 %).
+  // measured faster from one strip per CU on (prefill-64k-bound -1.5 %); four from four strips
+  // per CU on.
   const WalkShape shape = walk_shape(pairs, n_cu, p.S0 != nullptr && p.S0 == p.S_T);
-  const bool two = shape.two_strips;
+  const int strips = shape.strips;
   hipError_t e = launch_prep<BL == 2 * C>(p, stream, blk_off, ws);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
-    return p.out_bf16 ? launch_rec<uint16_t, BL>(p, stream, two, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws)
-                      : launch_rec<float, BL>(p, stream, two, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws);
+    return p.out_bf16 ? launch_rec<uint16_t, BL>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws)
+                      : launch_rec<float, BL>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws);
   };
   RecJobs jobs = {};
   const int P = n_segments(p);
