@@ -32,9 +32,9 @@
 //    operands need bf16's exponent range (fp16 would overflow at e^80), and are split into
 //    bf16 hi + lo pairs (three products) to keep 16 bits of precision. Off-diagonal factors
 //    are <= 1 and use fp16 (11-bit significand) directly.
-//  rec_kernel (one workgroup per sequence, head and strip of 16 or 32 value columns, serial
-//    over chunks): the fp32 state slice S[128][16 or 32] lives in MFMA accumulators for the
-//    whole sequence. Eight waves in two roles. Waves 0-3 own 32 key rows of the state each
+//  rec_kernel (one workgroup per sequence, head and strip of 16, 32 or 64 value columns,
+//    serial over chunks): the fp32 state slice S[128][16 .. 64] lives in MFMA accumulators for
+//    the whole sequence. Eight waves in two roles. Waves 0-3 own 32 key rows of the state each
 //    and carry the dependency chain: S <- S + Z + Psi S for their rows. Waves 4-7 compute the
 //    outputs Qhat S + Ohat of their 16 chunk rows from the same gathered state, off the chain.
 //    Columns of S evolve independently (the transition acts on the key side only), so
@@ -47,6 +47,10 @@
 // Z' = Z_a + Z_b + Psi_b Z_a, chunk b's outputs reading the state entering the pair through
 // Qhat_b (I + Psi_a) and Ohat_b + Qhat_b Z_a. Half the steps, and Psi' and Z' stored once
 // per 128 tokens.
+// With many pairs the walk streams its operands at what HBM delivers, and the block is stored
+// factored instead (W, Ktil^T, Utilde, Qbar, Aqk, e^{G_C}: 14 % fewer bytes, and prep skips
+// P, Qhat, Ohat, Phi and Z): rec_fact_kernel then forms U' = Utilde - W S per chunk and takes
+// both the state update and the outputs from it, with two exchanges per chunk instead of one.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_plan.h"
@@ -78,6 +82,20 @@ constexpr Layout layout(int BL) {
                 65536 + (BL / 16) * 12288};
 }
 static_assert(layout(64).block == 114688 && layout(128).block == 163840, "block sizes");
+
+// Factored block of one 64-token chunk (byte offsets): the walk forms U' = Utilde - W S itself
+// and takes both the state update and the outputs from it.
+//   w    W as A-operand fragments [token row tile rt][key k-step j]            16 KiB
+//   kt   Ktil^T as A-operand fragments [key row tile kt][token k-step jt]      16 KiB
+//   ut   Utilde fp32 result tiles [value tile ct][token row tile rt]           32 KiB
+//   qb   Qbar as A-operand fragments [key k-step j][token row tile rt]         16 KiB
+//   ah   Aqk high fp16 part, A-operand fragments [token k-step jt][row tile rt]  8 KiB
+//   al   Aqk low fp16 part, same order                                           8 KiB
+//   gam  e^{G_C} per key channel, fp32                                          512 B
+struct FLayout {
+  int w, kt, ut, qb, ah, al, gam, block;
+};
+constexpr FLayout flayout() { return FLayout{0, 16384, 32768, 65536, 81920, 90112, 98304, 98816}; }
 
 struct SeqInfo {
   int64_t tok0;  // first token of the sequence in the packed T axis
@@ -253,7 +271,7 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 // PAIRWISE replaces the dense diagonal tiles by the pairwise evaluation of the earlier
 // generation (each e^{G_r - G_j} formed per pair and channel, in fp32 on the vector ALUs),
 // which needs no bound on the decay: the ablation that measures what the bound buys.
-template <bool PAIRWISE, bool COMPOSE>
+template <bool PAIRWISE, bool COMPOSE, bool FACT = false>
 __global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
@@ -331,7 +349,8 @@ __global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
   const int64_t c_in = b_in * NGRP + grp;
   const int64_t tok0 = si.tok0 + c_in * C;
   const int Cn = (int)max((int64_t)0, min((int64_t)C, si.len - c_in * C));
-  uint8_t* blk = ws + ((size_t)(si.cid0 + b_in) * H + h) * LY.block;
+  static_assert(!(FACT && COMPOSE), "the factored block is one chunk");
+  uint8_t* blk = ws + ((size_t)(si.cid0 + b_in) * H + h) * (FACT ? flayout().block : LY.block);
 
   const int l = t & 63, gq = l >> 4, m = l & 15;
   const int row = 16 * w + m;
@@ -676,7 +695,7 @@ __global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
   //      fp16 hi + lo. M = T diag(beta) is lower triangular: entries of tile blocks right of the
   //      diagonal (never written) are taken as zero.
   half8 pfh[2], pfl[2];
-  {
+  if constexpr (!FACT) {
     floatx4 pt[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -717,6 +736,57 @@ __global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
       store_half_lds(reinterpret_cast<uint8_t*>(VBF), 2 * ks + hf, mfma_f16(v16, idf[hf], zero));
   }
   __syncthreads();
+  if constexpr (FACT) {
+    // ---- the factored block: Qbar and Aqk of row tile w as they are, Ktil^T fragments of key
+    //      tiles 2w and 2w + 1, e^{G_C}, and for the column tiles 2w, 2w + 1 of every chunk row
+    //      Utilde = M V (fp32 result tiles) and W = M Kbar computed transposed,
+    //      W^T = Kbar^T M^T, so that each lane holds four keys of one token: half of an
+    //      A-operand fragment of W (the other half is the other column tile).
+    constexpr FLayout FL = flayout();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      *reinterpret_cast<half8*>(blk + FL.qb + ((kk * 4 + w) * 64 + l) * 16) = qbar[kk];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      *reinterpret_cast<half8*>(blk + FL.ah + ((ks * 4 + w) * 64 + l) * 16) = ahi[ks];
+      *reinterpret_cast<half8*>(blk + FL.al + ((ks * 4 + w) * 64 + l) * 16) = alo[ks];
+    }
+#pragma unroll
+    for (int f = 4 * w; f < 4 * w + 4; ++f)  // fragment f: key tile f / 2, token k-step f % 2
+      *reinterpret_cast<half8*>(blk + FL.kt + (f * 64 + l) * 16) = KTL[f * 64 + l];
+    if (t < DK) reinterpret_cast<float*>(blk + FL.gam)[t] = GAMS[t];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      half8 mr[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int bb = 2 * kk + hf;
+          const floatx4 tv = *reinterpret_cast<const floatx4*>(&T32[(16 * rt + m) * AS + 16 * bb + 4 * gq]);
+          const floatx4 bv = *reinterpret_cast<const floatx4*>(&Bs[16 * bb + 4 * gq]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            mr[kk][4 * hf + ii] = static_cast<_Float16>(bb <= rt ? tv[ii] * bv[ii] : 0.f);
+        }
+      half8 wf;
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int ct = 2 * w + tc;
+        floatx4 dw = zero, du = zero;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          dw = mfma_f16(KBF[(ct * 2 + kk) * 64 + l], mr[kk], dw);
+          du = mfma_f16(mr[kk], VBF[(ct * 2 + kk) * 64 + l], du);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[4 * tc + i] = static_cast<_Float16>(dw[i]);
+        *reinterpret_cast<floatx4*>(blk + FL.ut + ((ct * 4 + rt) * 64 + l) * 16) = du;
+      }
+      *reinterpret_cast<half8*>(blk + FL.w + ((rt * 4 + w) * 64 + l) * 16) = wf;
+    }
+    return;
+  }
   // ---- row tile w: (P Kbar)^T = Kbar^T P^T, so that Qhat = Qbar - P Kbar comes out as
   //      A-operand fragments, and Ohat = P V as result tiles in the walk's accumulator layout.
   //      The second chunk of a composed block keeps both in registers for the composition.
@@ -1323,6 +1393,302 @@ __global__ __launch_bounds__(512) void rec_kernel(
   }
 }
 
+// The walk over factored blocks (one 64-token chunk per step). Per chunk, with S the state
+// entering it:
+//   U' = Utilde - W S,   o = Qbar S + Aqk U',   S <- Diag(e^{G_C}) S + Ktil^T U'.
+// State wave w holds key rows 32w .. 32w+31 of the strips. Its own rows, converted to fp16,
+// are exactly the B operand of k-step w, so it forms its part of W S over those keys without
+// any exchange: X_w = W[:, 32w..32w+31] S[32w..32w+31, :], four result tiles (one per token
+// row tile). The four parts meet in LDS; wave w adds them for token tile w and forms
+// U' = Utilde - X there (fp16 high and low parts); after a second barrier every wave reads
+// the whole U' as B operands for Ktil^T U' (its key rows) and for Aqk U' (the output waves,
+// with high and low parts of both). The output waves read the state entering the chunk, as
+// in rec_kernel, for Qbar S.
+template <typename TOut, int NT, bool CKPT>
+__global__ __launch_bounds__(512) void rec_fact_kernel(
+    RecJobs jobs, TOut* __restrict__ o, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, int T, int H, int n_seq, int64_t max_chunks,
+    const uint8_t* __restrict__ ws, float* __restrict__ ckpt, int ckpt_chunks, int ckpt_slots,
+    const int32_t* __restrict__ ckpt_off, const int32_t* __restrict__ order) {
+  constexpr FLayout FL = flayout();
+  constexpr int BL = C;
+  constexpr int NG = NSTRIP / NT;
+  constexpr int SR = DK + 8;
+  __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];  // state entering the chunk, fp16
+  __shared__ __align__(16) floatx4 xp[4][NT][4][64];     // parts of W S [wave][strip][token tile]
+  __shared__ __align__(16) half4 up[NT][4][2][64];       // U' [strip][token tile][high, low]
+
+  const RecJob job = jobs.job[blockIdx.x / jobs.blocks_per_job];
+  const int64_t c_lo = job.c_lo, c_hi = job.c_hi;
+  const float* __restrict__ S0 = job.mode == REC_OUTPUT ? job.S_in : nullptr;
+  float* __restrict__ S_T = job.S_out;
+  const bool transition = job.mode == REC_TRANSITION;
+  const int b = (int)(blockIdx.x % jobs.blocks_per_job);
+  const int xcd = b & 7, rest = b >> 3;
+  const int sg = rest % NG, r2 = rest / NG;
+  const int half = r2 % jobs.halves;
+  const int64_t pair = (int64_t)(r2 / jobs.halves) * 8 + xcd;
+  if (pair >= (int64_t)n_seq * H) return;
+  const int n = order ? order[pair / H] : (int)(pair / H), h = (int)(pair % H);
+  const SeqInfo si = seq_info<BL>(n, cu, chunk_off, T);
+  const int64_t nc = max((int64_t)0, min((si.len + BL - 1) / BL, max_chunks - si.cid0));
+  const int64_t c_end = min(nc, c_hi);
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int w = wave & 3;
+  const int l = t & 63, gq = l >> 4, nn = l & 15;
+  const int frag_off = l * 16;
+  const uint8_t* blk_base = ws + ((size_t)si.cid0 * H + h) * FL.block;
+  const size_t blk_step = (size_t)H * FL.block;
+  auto chunk_rsrc = [&](int64_t c) {
+    return make_rsrc(blk_base + min(c, c_end - 1) * blk_step, (int64_t)FL.block);
+  };
+  auto state_frag = [&](int bf, int nt, int j) { return lds_frag(&sx[bf][16 * nt + nn][32 * j], gq); };
+  // U' high (hl = 0) or low (1) parts as the B operand of token k-step jt: token tiles 2jt and
+  // 2jt + 1, the lane's own four rows of each
+  auto u_frag = [&](int nt, int jt, int hl) {
+    return frag_from_halves(up[nt][2 * jt][hl][l], up[nt][2 * jt + 1][hl][l]);
+  };
+  const int64_t ck_base =
+      ckpt_chunks > 0 ? (cu ? (int64_t)ckpt_off[n] : (int64_t)n * (T / (ckpt_chunks * BL))) : 0;
+  const int ck_every = CKPT && job.mode == REC_OUTPUT && half == 0 ? ckpt_chunks : 0;
+  if (half != 0) S_T = nullptr;
+
+  // ------------------------------------------------ output waves: chunk rows of JN row tiles
+  auto out_waves = [&](auto jn, int rt0, int rt1) {
+    constexpr int JN = decltype(jn)::value;
+    const int rts[2] = {rt0, rt1};
+    const int row_stride = H * DV;
+    int o_off[JN][NT][4];
+#pragma unroll
+    for (int j = 0; j < JN; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o_off[j][nt][i] = ((16 * rts[j] + 4 * gq + i) * row_stride + 16 * (NT * sg + nt) + nn) *
+                            (int)sizeof(TOut);
+    TOut* o_base = o + (si.tok0 * H + h) * DV;
+    const size_t tok_step = (size_t)BL * row_stride;
+    struct Ops {
+      half8 qb[JN][4];  // Qbar, key k-steps
+      half8 ah[JN][2], al[JN][2];  // Aqk high and low parts, token k-steps
+    };
+    Ops A, B;
+    auto load_q = [&](Ops& X, int64_t c) {
+      const rsrc_t r = chunk_rsrc(c);
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) X.qb[j][ks] = ld_frag(r, frag_off, FL.qb + (ks * 4 + rts[j]) * 1024);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          X.ah[j][jt] = ld_frag(r, frag_off, FL.ah + (jt * 4 + rts[j]) * 1024);
+          X.al[j][jt] = ld_frag(r, frag_off, FL.al + (jt * 4 + rts[j]) * 1024);
+        }
+      }
+    };
+    auto step = [&](Ops& X, int64_t c) {
+      const int bf = (int)(c & 1);
+      __syncthreads();  // A: the state entering chunk c is in sx[bf]
+      // Qbar S while the state waves form U'
+      floatx4 a0[JN][NT], a1[JN][NT];
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          a0[j][nt] = mfma_f16(X.qb[j][0], state_frag(bf, nt, 0), floatx4{0.f, 0.f, 0.f, 0.f});
+          a1[j][nt] = mfma_f16(X.qb[j][2], state_frag(bf, nt, 2), floatx4{0.f, 0.f, 0.f, 0.f});
+          a0[j][nt] = mfma_f16(X.qb[j][1], state_frag(bf, nt, 1), a0[j][nt]);
+          a1[j][nt] = mfma_f16(X.qb[j][3], state_frag(bf, nt, 3), a1[j][nt]);
+        }
+      __syncthreads();  // B: U' of chunk c is in up
+      floatx4 acc[JN][NT];
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const half8 uh = u_frag(nt, jt, 0), ul = u_frag(nt, jt, 1);
+            a0[j][nt] = mfma_f16(X.ah[j][jt], uh, a0[j][nt]);
+            a1[j][nt] = mfma_f16(X.ah[j][jt], ul, a1[j][nt]);
+            a1[j][nt] = mfma_f16(X.al[j][jt], uh, a1[j][nt]);
+          }
+          acc[j][nt] = a0[j][nt] + a1[j][nt];
+        }
+      load_q(X, c + 2);
+      const int64_t rows = min((int64_t)BL, si.len - c * BL);
+      const rsrc_t ro = make_rsrc(o_base + c * tok_step, ((rows - 1) * row_stride + DV) * (int64_t)sizeof(TOut));
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (sizeof(TOut) == 4)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][nt][i]), ro, o_off[j][nt][i], 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[j][nt][i]), ro, o_off[j][nt][i], 0, 0);
+          }
+    };
+    if (c_end > c_lo) {
+      load_q(A, c_lo);
+      load_q(B, c_lo + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    int64_t c = c_lo;
+    for (; c + 1 < c_end; c += 2) {
+      step(A, c);
+      step(B, c + 1);
+    }
+    if (c < c_end) step(A, c);
+  };
+
+  if (wave < 4) {
+    // ------------------------------------------------ state waves: key rows 32w .. 32w+31
+    __builtin_amdgcn_s_setprio(2);
+    const int64_t s_base = ((int64_t)n * H + h) * DK * DV;
+    int col[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) col[nt] = 16 * (NT * sg + nt) + nn;
+    floatx4 s[NT][2];  // rows 32w + 16u + 4gq + i, columns col[nt]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 32 * w + 16 * u + 4 * gq + i;
+          s[nt][u][i] = transition ? (r == col[nt] ? 1.f : 0.f)
+                                   : (S0 ? S0[s_base + (int64_t)r * DV + col[nt]] : 0.f);
+        }
+    // Operands two chunks ahead in three register sets used in rotation, as in rec_kernel.
+    // The transition walk has V = 0: its Utilde loads read an empty range (zeros).
+    const int ut_bytes = transition ? 0 : FL.block;
+    struct Ops {
+      half8 wf[4];     // W fragments of token tiles 0..3, key k-step w
+      half8 kf[2][2];  // Ktil^T fragments of key tiles 2w + u, token k-steps jt
+      floatx4 ut[NT];  // Utilde of token tile w, value tiles of the strips
+      floatx4 gm[2];   // e^{G_C} of key rows 32w + 16u + 4gq .. + 3
+    };
+    Ops A, B, Cs;
+    auto load_ops = [&](Ops& X, int64_t c) {
+      const uint8_t* base = blk_base + min(c, c_end - 1) * blk_step;
+      const rsrc_t r = make_rsrc(base, (int64_t)FL.block);
+      const rsrc_t ru = make_rsrc(base, (int64_t)ut_bytes);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) X.ut[nt] = ld_tile(ru, frag_off, FL.ut + ((NT * sg + nt) * 4 + w) * 1024);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) X.wf[rt] = ld_frag(r, frag_off, FL.w + (rt * 4 + w) * 1024);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) X.kf[u][jt] = ld_frag(r, frag_off, FL.kt + ((2 * w + u) * 2 + jt) * 1024);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        X.gm[u] = ld_tile(r, (32 * w + 16 * u + 4 * gq) * 4, FL.gam);
+    };
+    auto step = [&](Ops& X, Ops& Y, int64_t c) {
+      const int bf = (int)(c & 1);
+      // -- the state entering the chunk: fp16 for the output waves, and this wave's own rows
+      //    as the B operand of key k-step w
+      half8 sw[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          half4 hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(s[nt][u][i]);
+          *reinterpret_cast<half4*>(&sx[bf][16 * nt + nn][32 * w + 16 * u + 4 * gq]) = hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sw[nt][4 * u + i] = hv[i];
+        }
+      // -- this wave's part of W S, token tiles 0..3
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          xp[w][nt][rt][l] = mfma_f16(X.wf[rt], sw[nt], floatx4{0.f, 0.f, 0.f, 0.f});
+      load_ops(Y, c + 2);
+      __syncthreads();  // A
+      // -- U' of token tile w: Utilde - (sum of the four parts), high and low fp16 parts
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const floatx4 x = (xp[0][nt][w][l] + xp[1][nt][w][l]) + (xp[2][nt][w][l] + xp[3][nt][w][l]);
+        const floatx4 uu = X.ut[nt] - x;
+        half4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = static_cast<_Float16>(uu[i]);
+          lo[i] = static_cast<_Float16>(uu[i] - static_cast<float>(hi[i]));
+        }
+        up[nt][w][0][l] = hi;
+        up[nt][w][1][l] = lo;
+      }
+      __syncthreads();  // B
+      // -- S <- Diag(e^{G_C}) S + Ktil^T U' for this wave's rows
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const half8 u0 = u_frag(nt, 0, 0), u1 = u_frag(nt, 1, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          floatx4 seed;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) seed[i] = s[nt][u][i] * X.gm[u][i];
+          seed = mfma_f16(X.kf[u][0], u0, seed);
+          s[nt][u] = mfma_f16(X.kf[u][1], u1, seed);
+        }
+      }
+      if (CKPT && ck_every > 0 && (c + 1) % ck_every == 0 && (c + 1) * BL <= si.len) {
+        const int64_t slot = ck_base + (c + 1) / ck_every - 1;
+        if (slot < ckpt_slots) {
+          float* dst = ckpt + (slot * H + h) * DK * DV;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dst[(int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+        }
+      }
+    };
+    if (c_end > c_lo) {
+      load_ops(A, c_lo);
+      load_ops(B, c_lo + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    int64_t c = c_lo;
+    for (; c + 2 < c_end; c += 3) {
+      step(A, Cs, c);
+      step(B, A, c + 1);
+      step(Cs, B, c + 2);
+    }
+    if (c < c_end) step(A, Cs, c);
+    if (c + 1 < c_end) step(B, A, c + 1);
+    if (S_T) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S_T[s_base + (int64_t)(32 * w + 16 * u + 4 * gq + i) * DV + col[nt]] = s[nt][u][i];
+    }
+  } else if (job.mode != REC_OUTPUT || (jobs.halves == 2 && (w >> 1) != half)) {
+    // ------------------------------------------------ no outputs: keep the barriers in step
+    for (int64_t c = c_lo; c < c_end; ++c) {
+      __syncthreads();
+      __syncthreads();
+    }
+  } else {
+    // one row tile per output wave: tile w (each workgroup of a split pair takes half of them)
+    out_waves(IntC<1>{}, w, 0);
+  }
+}
+
 // Entry state of the next segment from the previous one's: S_next = Phi S_in + Z, per
 // (sequence, head), fp32. One workgroup per (sequence, head, 16-column strip); Phi is streamed
 // through LDS in 32-column slabs.
@@ -1369,6 +1735,9 @@ int64_t max_blocks(const ChunkPlan& p) {
   return p.cu_seqlens ? per + p.n_seq : (int64_t)p.B * per;
 }
 
+// The blocks come first, one slot of layout(BL).block bytes per (block, head); the factored
+// blocks (flayout().block bytes, one-chunk walks only) are packed at their own stride inside
+// the same span, so the tables after it do not depend on the block format.
 size_t block_table_offset(const ChunkPlan& p) {
   return (size_t)max_blocks(p) * p.H * layout(walk_block(p)).block;
 }
@@ -1418,10 +1787,30 @@ hipError_t launch_rec(const ChunkPlan& p, hipStream_t stream, int strips, int ha
   return hipGetLastError();
 }
 
-template <bool COMPOSE>
+template <typename TOut>
+hipError_t launch_rec_fact(const ChunkPlan& p, hipStream_t stream, int strips, int halves,
+                           int64_t pairs, RecJobs jobs, int n_jobs, const int32_t* blk_off,
+                           const int32_t* ckpt_off, const int32_t* order, uint8_t* ws) {
+  jobs.halves = halves;
+  jobs.blocks_per_job = ((pairs + 7) / 8) * 8 * (NSTRIP / strips) * halves;
+  const dim3 grid((unsigned)(jobs.blocks_per_job * n_jobs)), block(512);
+  const int ck_blocks = p.ckpt ? p.ckpt_every / C : 0;
+  auto kern = p.ckpt ? (strips == 4   ? rec_fact_kernel<TOut, 4, true>
+                        : strips == 2 ? rec_fact_kernel<TOut, 2, true>
+                                      : rec_fact_kernel<TOut, 1, true>)
+                     : (strips == 4   ? rec_fact_kernel<TOut, 4, false>
+                        : strips == 2 ? rec_fact_kernel<TOut, 2, false>
+                                      : rec_fact_kernel<TOut, 1, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, jobs, static_cast<TOut*>(p.o), p.cu_seqlens,
+                     blk_off, p.T, p.H, p.n_seq, max_blocks(p), ws, p.ckpt, ck_blocks,
+                     p.ckpt_slots, ckpt_off, order);
+  return hipGetLastError();
+}
+
+template <bool COMPOSE, bool FACT = false>
 hipError_t launch_prep(const ChunkPlan& p, hipStream_t stream, const int32_t* blk_off, uint8_t* ws) {
   const int64_t blocks = max_blocks(p) * p.H;
-  auto kern = p.pairwise_diag ? prep_kernel<true, COMPOSE> : prep_kernel<false, COMPOSE>;
+  auto kern = p.pairwise_diag ? prep_kernel<true, COMPOSE, FACT> : prep_kernel<false, COMPOSE, FACT>;
   if (blocks > 0)
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(COMPOSE ? 512 : 256), 0, stream,
                        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
@@ -1453,9 +1842,19 @@ hipError_t launch_fast(const ChunkPlan& p, hipStream_t stream) {
   // per CU on.
   const WalkShape shape = walk_shape(pairs, n_cu, p.S0 != nullptr && p.S0 == p.S_T);
   const int strips = shape.strips;
-  hipError_t e = launch_prep<BL == 2 * C>(p, stream, blk_off, ws);
+  // From one 16-column strip per CU on, the walk streams its operands at what HBM delivers
+  // and its chain latency is hidden: then the factored block (98,816 of each block slot's
+  // 114,688 bytes, and fewer products in prep) pays for the walk's second exchange per chunk
+  // (prefill-64k-bound -2.7 %, varlen-16 -8.7 %). With fewer pairs the walk is latency bound
+  // and one exchange per chunk wins.
+  const bool fact = BL == C && strips >= 2;
+  hipError_t e = fact ? launch_prep<false, true>(p, stream, blk_off, ws)
+                      : launch_prep<BL == 2 * C>(p, stream, blk_off, ws);
   if (e != hipSuccess) return e;
   auto rec = [&](const RecJobs& jobs, int n_jobs, int halves) {
+    if (fact)
+      return p.out_bf16 ? launch_rec_fact<uint16_t>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws)
+                        : launch_rec_fact<float>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws);
     return p.out_bf16 ? launch_rec<uint16_t, BL>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws)
                       : launch_rec<float, BL>(p, stream, strips, halves, pairs, jobs, n_jobs, blk_off, ckpt_off, order, ws);
   };

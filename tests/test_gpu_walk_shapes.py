@@ -1,14 +1,15 @@
-"""Workgroup shapes of the matrix-core walk against the oracle. From the number of
-(sequence, head) pairs the library picks 1, 2 or 4 strips of 16 state columns per workgroup
-(four once there are at least four strips per CU, two from one per CU); each shape is run here
-with its outputs, final states, checkpoints, the final state written over S0, and a segmented
-walk."""
+"""Workgroup shapes and block formats of the matrix-core walk against the oracle. From the
+number of (sequence, head) pairs the library picks 1, 2 or 4 strips of 16 state columns per
+workgroup (four once there are at least four strips per CU, two from one per CU), and from one
+strip per CU on the factored block (the walk forms U' = Utilde - W S per chunk). Each shape is
+run here with its outputs in fp32 and bf16, run to run bitwise, final states, checkpoints,
+the final state written over S0, and a segmented walk."""
 import numpy as np
 import pytest
 
 import oracle
 from gated_delta_rule_59_amd import inputs
-from tests.gpu_util import TAU, assert_parity, host, kda_inputs_dev
+from tests.gpu_util import TAU, assert_parity, host, kda_inputs_dev, rms
 from tests.test_gpu_checkpoints import expected_checkpoints, seq_lengths
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +32,8 @@ def strips_per_workgroup(pairs, n_cu):
     return 4 if strips >= 4 * n_cu else 2 if strips >= n_cu else 1
 
 
-# (sequences, heads): 8 pairs, 40 pairs and 160 pairs on a 256-CU GPU
+# (sequences, heads): 8 pairs (one strip, Psi/Z blocks), 40 pairs (two strips) and 160 pairs
+# (four strips), both with factored blocks, on a 256-CU GPU
 SHAPES = {"few pairs": (4, 2), "two strips": (20, 2), "four strips": (40, 4)}
 
 
@@ -41,8 +43,9 @@ def test_walk_shapes(name):
     from gated_delta_rule_59_amd import binding
     n_seq, H = SHAPES[name]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    print(f"{name}: {n_seq * H} pairs, {strips_per_workgroup(n_seq * H, n_cu)} strip(s) per "
-          f"workgroup on {n_cu} CUs", flush=True)
+    strips = strips_per_workgroup(n_seq * H, n_cu)
+    print(f"{name}: {n_seq * H} pairs, {strips} strip(s) per workgroup on {n_cu} CUs, "
+          f"{'factored' if strips >= 2 else 'Psi/Z'} blocks", flush=True)
     x = packed_case(n_seq, H, seed=len(name))
     o_ref, s_ref = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0, cu_seqlens=x.cu_seqlens)
     q, k, v, g, beta, S0, cu = kda_inputs_dev(x)
@@ -50,9 +53,17 @@ def test_walk_shapes(name):
     # outputs and final state, one chunk per walk step so that checkpoints every 64 tokens
     # take the same walk
     o, s = binding.chunk_fwd(q, k, v, g, beta, S0, cu, walk64=True)
+    o_again, s_again = binding.chunk_fwd(q, k, v, g, beta, S0, cu, walk64=True)
     torch.cuda.synchronize()
     assert_parity(host(o), o_ref, TAU["bf16"], f"{name} o")
     assert_parity(host(s), s_ref, TAU["bf16"], f"{name} S_T")
+    assert torch.equal(o, o_again) and torch.equal(s, s_again)  # deterministic
+
+    # bf16 outputs: at most half an ulp (2^-8 relative) more than the fp32-output error
+    o16, _ = binding.chunk_fwd(q, k, v, g, beta, S0, cu, walk64=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got16 = host(o16)
+    assert (np.abs(got16 - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + TAU["bf16"] * rms(o_ref)).all()
 
     # checkpoints every 64 tokens; the outputs are unaffected by them
     every = 64
