@@ -286,7 +286,8 @@ class Prefill:
 
 
 def roofline(fig, bytes_per_launch, traffic):
-    return {"kernel": "kda_chunk_fwd launch (prep_kernel + rec_kernel)", "bound": "hbm",
+    return {"kernel": "kda_chunk_fwd launch (prep_kernel + the walk: rec_kernel, or rec_fact_kernel "
+                      "with the factored block from 32 (sequence, head) pairs on)", "bound": "hbm",
             "achieved": fig["alg_GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": fig["alg_hbm_frac"], "traffic": traffic,
             "bytes_per_launch": bytes_per_launch,
