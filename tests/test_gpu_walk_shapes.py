@@ -2,8 +2,8 @@
 number of (sequence, head) pairs the library picks 1, 2 or 4 strips of 16 state columns per
 workgroup (four once there are at least four strips per CU, two from one per CU), and from one
 strip per CU on the factored block (the walk forms U' = Utilde - W S per chunk). Each shape is
-run here with its outputs in fp32 and bf16, run to run bitwise, final states, checkpoints,
-the final state written over S0, and a segmented walk."""
+run here with its outputs in fp32 and bf16, run to run bitwise, final states, the pairwise
+diagonal tiles, checkpoints, the final state written over S0, and a segmented walk."""
 import numpy as np
 import pytest
 
@@ -64,6 +64,12 @@ def test_walk_shapes(name):
     torch.cuda.synchronize()
     got16 = host(o16)
     assert (np.abs(got16 - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + TAU["bf16"] * rms(o_ref)).all()
+
+    # the diagonal tiles evaluated pairwise (the ablation's prep) feed the same walk
+    o_pw, s_pw = binding.chunk_fwd(q, k, v, g, beta, S0, cu, walk64=True, pairwise_diag=True)
+    torch.cuda.synchronize()
+    assert_parity(host(o_pw), o_ref, TAU["bf16"], f"{name} o, pairwise diagonal tiles")
+    assert_parity(host(s_pw), s_ref, TAU["bf16"], f"{name} S_T, pairwise diagonal tiles")
 
     # checkpoints every 64 tokens; the outputs are unaffected by them
     every = 64
