@@ -26,27 +26,38 @@ def packed_case(n_seq, H, seed):
     return inputs.KDAInputs(wl, q, k, v, g, beta, S0, cu)
 
 
+def dense_case(B, T, H, seed):
+    q, k, v, g, beta = inputs.draw_activations((12, seed), B, T, H, 128, 128, "bf16")
+    S0 = inputs.draw_state((12, seed), B, H, 128, 128)
+    wl = inputs.Workload(f"walk-shape-dense-{B}x{T}x{H}", 1, H, 128, 128, 64, "bf16", B=B, T=T)
+    return inputs.KDAInputs(wl, q, k, v, g, beta, S0)
+
+
 def strips_per_workgroup(pairs, n_cu):
     """The launch-shape rule, restated: strips of one walk workgroup."""
     strips = pairs * 8
     return 4 if strips >= 4 * n_cu else 2 if strips >= n_cu else 1
 
 
-# (sequences, heads): 8 pairs (one strip, Psi/Z blocks), 40 pairs (two strips) and 160 pairs
-# (four strips), both with factored blocks, on a 256-CU GPU
-SHAPES = {"few pairs": (4, 2), "two strips": (20, 2), "four strips": (40, 4)}
+# On a 256-CU GPU: 8 pairs (one strip, Psi/Z blocks); 40 and 42 pairs (two strips) and 160 pairs
+# (four strips) with factored blocks, 42 leaving the last group of eight pairs part empty; a
+# dense batch of 20 sequences of 150 tokens (40 pairs).
+SHAPES = {"few pairs": lambda: packed_case(4, 2, 10), "two strips": lambda: packed_case(20, 2, 11),
+          "42 pairs": lambda: packed_case(21, 2, 12), "four strips": lambda: packed_case(40, 4, 13),
+          "dense 20 x 150": lambda: dense_case(20, 150, 2, 14)}
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_walk_shapes(name):
     import torch
     from gated_delta_rule_59_amd import binding
-    n_seq, H = SHAPES[name]
+    x = SHAPES[name]()
+    H = x.wl.H
+    n_seq = len(seq_lengths(x))
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     strips = strips_per_workgroup(n_seq * H, n_cu)
     print(f"{name}: {n_seq * H} pairs, {strips} strip(s) per workgroup on {n_cu} CUs, "
           f"{'factored' if strips >= 2 else 'Psi/Z'} blocks", flush=True)
-    x = packed_case(n_seq, H, seed=len(name))
     o_ref, s_ref = oracle.kda_reference(x.q, x.k, x.v, x.g, x.beta, x.S0, cu_seqlens=x.cu_seqlens)
     q, k, v, g, beta, S0, cu = kda_inputs_dev(x)
 
