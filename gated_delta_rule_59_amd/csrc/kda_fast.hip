@@ -203,11 +203,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // gfx950 the last dword of some lanes was then read after the rewrite (wrong workspace values,
 // intermittently).
 
-// x from lane m - S of the same 16-lane DPP row (0 for m < S).
-template <int S>
-__device__ __forceinline__ float row_shr(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + S, 0xF, 0xF, true));
-}
 // 2^x for x in [-116, 0], the range of a decay factor across one 16-token tile (each step's
 // log-decay is >= -5): the hardware exp2 is exact to its ulp bound there and needs none of
 // the scaling that exp2f adds for arguments below -126.
@@ -228,14 +223,6 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, r);
 }
-// Inclusive prefix sum over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row_scan(float x) {
-  x += row_shr<1>(x);
-  x += row_shr<2>(x);
-  x += row_shr<4>(x);
-  x += row_shr<8>(x);
-  return x;
-}
 
 __device__ __forceinline__ half8 frag_from_halves(const half4& a, const half4& b) {
   half8 f;
@@ -255,10 +242,9 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* rowp, int gq) {
 
 // One workgroup per (chunk, head); wave a owns row tile a (chunk rows 16a .. 16a+15). In the
 // MFMA fragment layout lane l of wave a holds row 16a + (l & 15) and, for each of the four
-// 32-channel k-steps, the eight channels 32 ks + kslot(l >> 4, i). The 16 lanes that share
-// l >> 4 form one DPP row and hold the same channels of the tile's 16 rows, so the per-tile
-// cumulative decay is a 16-lane scan. Every per-element quantity is formed once, in
-// registers, in that layout:
+// 32-channel k-steps, the eight channels 32 ks + kslot(l >> 4, i). The per-tile cumulative
+// decay is a prefix sum over the tile's 16 rows, formed on the matrix cores in that same
+// layout. Every per-element quantity is formed once, in registers, in that layout:
 //   rf = e^{G_r - ref_a}   (ref_a = G at the last token before tile a)   in [e^-80, 1]
 //   cf = e^{Gend_a - G_r}  (Gend_a = G at the last token of tile a)       in [e^-80, 1]
 // The row operand of tile a is k rf (q rf), its diagonal column operand k / rf (in [1, e^80]
@@ -394,13 +380,39 @@ __global__ __launch_bounds__(COMPOSE ? 512 : 256, 2) void prep_kernel(
         qraw[ks][hf] = ld_in(rs_q, ks, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // ---- cumulative log-decay within the row tile (log2 units): a scan over the DPP row
+  // ---- cumulative log-decay within the row tile (log2 units), on the matrix cores. The
+  //      identity product turns each 16-channel half of a k-step of g channel-major (a lane then
+  //      holds four rows of one channel; exact: bf16 values times one); the product of that with
+  //      the transposed 16 x 16 lower triangle of ones, g^T L^T, is every row's inclusive prefix
+  //      sum, in the inputs' own layout (row m, channels 16 hf + 4 gq + i).
   float gsa[4][8];
+  {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x8 idb[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      gsa[ks][i] = row_scan(bf16_bits_to_f32(graw[ks][i >> 2][i & 3]) * kLog2e);
+      for (int i = 0; i < 8; ++i)
+        idb[hf][i] = static_cast<__bf16>((i >> 2) == hf && 4 * gq + (i & 3) == m ? 1.f : 0.f);
+    bf16x4 ltri;  // L^T: rows 4 gq + i, column m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ltri[i] = static_cast<__bf16>(4 * gq + i <= m ? 1.f : 0.f);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 gf = __builtin_bit_cast(bf16x8, u16x8{graw[ks][0][0], graw[ks][0][1], graw[ks][0][2], graw[ks][0][3],
+                                                         graw[ks][1][0], graw[ks][1][1], graw[ks][1][2], graw[ks][1][3]});
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const floatx4 tr = mfma_bf16(gf, idb[hf], floatx4{0.f, 0.f, 0.f, 0.f});
+        bf16x4 gt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gt[i] = static_cast<__bf16>(tr[i]);
+        const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gt, ltri, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gsa[ks][4 * hf + i] = d[i] * kLog2e;
+      }
+    }
+  }
   auto scan_ks = [&](int ks, float (&gk)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) gk[i] = gsa[ks][i];
