@@ -7,7 +7,9 @@ forms the recurrence reduces to:
   - beta = 1 with keys of exactly unit norm: the write is exact, S_t^T k_t = v_t for every t
     and any g (the decayed state's prediction of v_t is replaced by v_t itself);
   - g = -5 on every key channel: every 16-token tile's cumulative log-decay is exactly -80,
-    the edge of the range the decay bound guarantees.
+    the edge of the range the decay bound guarantees;
+  - gates of mixed magnitude (-5, -1e-3, -1e-6 and 0 at random per element): the per-tile
+    prefix sums add terms six orders of magnitude apart.
 Both prefill paths (the matrix-core path and the fp32 path), the decode step and speculative
 drafts are covered."""
 import numpy as np
@@ -66,8 +68,16 @@ def floor():
     return x
 
 
+def mixed():
+    x = inputs.make_prefill(1, T=T, H=H)
+    rng = np.random.default_rng([0, 7, 12])
+    levels = np.array([inputs.GATE_FLOOR, -1e-3, -1e-6, 0.0], np.float32)
+    x.g = inputs.round_to_bf16(levels[rng.integers(0, 4, x.g.shape)])
+    return x
+
+
 CASES = {"beta=0": beta0, "beta=0 g=0": identity, "g=0": g0, "beta=1 unit k": beta1,
-         "g=-5 everywhere": floor}
+         "g=-5 everywhere": floor, "mixed magnitudes": mixed}
 
 
 def run(x, generic):
