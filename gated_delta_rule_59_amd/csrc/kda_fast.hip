@@ -1127,13 +1127,14 @@ __global__ __launch_bounds__(512) void rec_kernel(
   // followed by one barrier: the state strips entering the chunk (all 128 key rows), which the
   // state waves need whole for Psi S and the output waves for Qhat S. They are stored
   // column-major ([column][row]) so the rows a lane needs for a B operand are contiguous, with
-  // rows padded by 8 halves against bank conflicts, in two buffers used by alternate chunks:
+  // rows padded by 4 halves (the fragment reads of 16 lanes then fall into distinct banks; 8
+  // halves measured 2-way bank conflicts), in two buffers used by alternate chunks:
   // the buffer of chunk c is read between barrier c and barrier c + 1, and written again only
   // for chunk c + 2, after barrier c + 1.
   constexpr Layout LY = layout(BL);
   constexpr int RT = BL / 16;      // row tiles of a chunk
   constexpr int NG = NSTRIP / NT;  // strip groups per (sequence, head)
-  constexpr int SR = DK + 8;
+  constexpr int SR = DK + 4;  // 66 words per row: conflict-free fragment reads
   __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];
 
   const RecJob job = jobs.job[blockIdx.x / jobs.blocks_per_job];
@@ -1425,7 +1426,7 @@ __global__ __launch_bounds__(512) void rec_fact_kernel(
   constexpr FLayout FL = flayout();
   constexpr int BL = C;
   constexpr int NG = NSTRIP / NT;
-  constexpr int SR = DK + 8;
+  constexpr int SR = DK + 4;  // 66 words per row: conflict-free fragment reads
   __shared__ __align__(16) _Float16 sx[2][NT * 16][SR];  // state entering the chunk, fp16
   __shared__ __align__(16) floatx4 xp[4][NT][4][64];     // parts of W S [wave][strip][token tile]
   __shared__ __align__(16) half4 up[NT][4][2][64];       // U' [strip][token tile][high, low]
