@@ -53,7 +53,7 @@ def flops_per_token_head(C=64, d=128):
 
 def bytes_per_token_head(d=128, in_bytes=2, out_bytes=2):
     """Minimal bytes: q, k, g, v (d each) and beta read once, o written once. The default is
-    the bf16-sized output; out_bytes=4 gives the count for the fp32 o this build writes."""
+    the bf16-sized output; out_bytes=4 gives the count for the fp32 o the library writes."""
     return 4 * d * in_bytes + in_bytes + d * out_bytes
 
 
@@ -293,7 +293,7 @@ def roofline(fig, bytes_per_launch, traffic):
             "bytes_per_launch": bytes_per_launch,
             "bytes_count": "minimal: bf16 q, k, v, g, beta read once and a bf16-sized o written "
                            "once (1,282 B per token-head), plus S0 read and S_T written once; "
-                           "fp32_o_* fields count the 4-byte o this build writes (1,538 B)"}
+                           "fp32_o_* fields count the 4-byte o the library writes (1,538 B)"}
 
 
 def bench_extra(name, stream, do_parity, launches=10):
@@ -426,7 +426,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); KDA "
+        print(f"bench.py: runs on one GPU only (asked for {args.gpus}); KDA "
               "prefill and decode shard over independent (sequence, head) pairs with no "
               "communication, so N GPUs would each run this same single-GPU workload.",
               file=sys.stderr)

@@ -67,7 +67,7 @@ typedef enum {
     KDA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
     KDA_ERR_BAD_SHAPE = 2,    /* sizes out of range or inconsistent */
     KDA_ERR_BAD_DTYPE = 3,    /* dtype combination not offered */
-    KDA_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement */
+    KDA_ERR_UNSUPPORTED = 4,  /* valid request the library does not implement */
     KDA_ERR_DECAY_RANGE = 5,  /* KDA_CHECK=1 found g outside [-5, 0] or beta outside [0, 1] */
     KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than kda_chunk_fwd_workspace_bytes() */
     KDA_ERR_HIP = 7,          /* a HIP runtime call or kernel launch failed */

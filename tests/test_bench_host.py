@@ -17,7 +17,7 @@ def test_algorithmic_counts():
     assert bench.flops_per_token_head() == 5 * 64 * 128 + 6 * 128 * 128 == 139264
     # minimal bytes: q, k, g, v and beta in bf16 read once, a bf16-sized o written once
     assert bench.bytes_per_token_head() == 4 * 128 * 2 + 2 + 128 * 2 == 1282
-    # the same with the fp32 o this build writes
+    # the same with the fp32 o the library writes
     assert bench.bytes_per_token_head(out_bytes=4) == 1538
     # S0 read and S_T written once, fp32: 128 KiB per (sequence, head)
     assert bench.state_bytes(1, 16) == 16 * 2 * 4 * 128 * 128
